@@ -1,0 +1,183 @@
+/*
+ * vpe.h - C ABI of the vocab-parallel embedding / LM-head library (libvpe.so).
+ *
+ * One tensor-parallel rank's share of the two vocabulary-sharded layers of a
+ * decoder LLM, as the nano-vllm pages describe them:
+ *   - the embedding: the table [V, D] is split by rows into tp contiguous
+ *     shards; a shard looks up only the ids it owns and returns zero rows for
+ *     the rest, and the ranks' partial outputs are summed;
+ *   - the LM head: the same [V/tp, D] shard produces the logits of the words
+ *     it owns, and the ranks' logits are concatenated along the vocabulary.
+ *
+ * Sources (page and section):
+ *   [TP-vocab]  devpress.csdn.net/amd/6a3de260..., nano-vllm article on the
+ *               vocab and head split: section 3 (VocabParallelEmbedding),
+ *               section 4 (ParallelLMHead), section 6 (integration check).
+ *   [TP-math]   devpress.csdn.net/amd/6a3b3792..., nano-vllm article on the
+ *               mathematics of tensor parallelism: section 5.
+ *   [vLLM-1.1]  blog.xiaohansong.com, "从零实现 vLLM (1.1)：并行词嵌入
+ *               VocabParallelEmbedding": the rank-by-rank walkthrough and the
+ *               nano-vllm source analysis.
+ *   [Guide-3.3] caomaolufei.github.io AIInfraGuide, "3.3 模型骨架与核心算子",
+ *               section 6 (vocab-parallel Embedding and LMHead).
+ *
+ * Conventions for every call:
+ *   - Pointers named as device pointers must point to device memory (or memory
+ *     the device can address) that the caller allocated and owns; the library
+ *     allocates nothing, keeps no state between calls and never synchronises.
+ *   - Tensors are dense and row-major unless a stride is given.
+ *   - `stream` is a hipStream_t (NULL = the default stream). Work is enqueued
+ *     on it and the call returns without waiting for it.
+ *   - Arguments are validated on the host before anything is enqueued; a
+ *     non-VPE_OK status means nothing was enqueued, except VPE_ERR_LAUNCH,
+ *     which reports a launch the HIP runtime refused.
+ *   - Values held in device memory (ids, cu_seqlens) are not validated: their
+ *     out-of-range cases have defined results, stated per call.
+ *   - Calls are thread-safe (no shared mutable state).
+ */
+#ifndef VPE_H
+#define VPE_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum vpe_status {
+    VPE_OK = 0,
+    VPE_ERR_NULL = 1,   /* a required pointer is NULL */
+    VPE_ERR_SHAPE = 2,  /* a size is negative, zero where it may not be, or too large */
+    VPE_ERR_DTYPE = 3,  /* unknown element or index type */
+    VPE_ERR_ALIGN = 4,  /* a pointer is not aligned to its element size */
+    VPE_ERR_SHARD = 5,  /* tp split invalid: V % tp != 0, rank outside [0, tp) */
+    VPE_ERR_LAUNCH = 6, /* the HIP runtime refused a kernel launch */
+    VPE_ERR_RANGE = 7   /* an output column range does not fit its row stride */
+} vpe_status;
+
+typedef enum vpe_dtype {
+    VPE_F32 = 0,  /* IEEE binary32 */
+    VPE_BF16 = 1  /* bfloat16: the upper 16 bits of a binary32 */
+} vpe_dtype;
+
+typedef enum vpe_itype {
+    VPE_I32 = 0,  /* int32 token ids */
+    VPE_I64 = 1   /* int64 token ids */
+} vpe_itype;
+
+/* Largest number of partials vpe_sum_partials accepts in one call. */
+#define VPE_MAX_PARTS 64
+
+/*
+ * Shard ownership of rank `tp_rank` among `tp_size` ranks over a vocabulary of
+ * `vocab` ids ([TP-vocab] section 3 constructor; [vLLM-1.1] source analysis):
+ * shard size R = vocab / tp_size, *vocab_start = R * tp_rank,
+ * *vocab_end = *vocab_start + R.  Ranks own contiguous blocks in rank order.
+ *
+ * Host-only; touches no device.  Pointers are host pointers.
+ * Errors: VPE_ERR_NULL (output pointer NULL); VPE_ERR_SHARD (vocab < 1,
+ * tp_size < 1, tp_rank outside [0, tp_size), or vocab % tp_size != 0 -- the
+ * vocabulary must split evenly, as [vLLM-1.1] asserts).
+ */
+vpe_status vpe_shard_range(int64_t vocab, int32_t tp_size, int32_t tp_rank,
+                           int64_t *vocab_start, int64_t *vocab_end);
+
+/*
+ * One shard's masked embedding lookup, steps 1-4 of [TP-vocab] section 3
+ * (mask, shift to a local index, look up, clear rows the shard does not own);
+ * [vLLM-1.1] steps 1-4; [Guide-3.3] section 6:
+ *
+ *   out[i, :] = weight[ids[i] - vocab_start, :]  if vocab_start <= ids[i] < vocab_start + shard_rows
+ *             = all-zero bits (+0.0)             otherwise
+ *
+ * ids     device, [n] of `itype`, any values (ids outside the shard, negative
+ *         ids and ids >= V all give zero rows; no row is read for them).
+ * weight  device, [shard_rows, dim] of `dt`: the shard (rows vocab_start ..
+ *         vocab_start + shard_rows - 1 of the full table).
+ * out     device, [n, dim] of `dt`; must not overlap ids or weight.
+ * The copy is bit-exact (no arithmetic touches the values).
+ * n == 0 is a no-op.  The full (tp = 1) lookup is vocab_start = 0,
+ * shard_rows = V.
+ * Errors: VPE_ERR_NULL, VPE_ERR_SHAPE (n < 0, dim < 1, shard_rows < 1),
+ * VPE_ERR_DTYPE, VPE_ERR_ALIGN (a pointer not aligned to its element size).
+ */
+vpe_status vpe_embed(const void *ids, vpe_itype itype, int64_t n,
+                     const void *weight, vpe_dtype dt, int64_t shard_rows, int64_t dim,
+                     int64_t vocab_start, void *out, void *stream);
+
+/*
+ * Step 5 of [TP-vocab] section 3, the all-reduce sum of the ranks' partial
+ * embeddings, done on one device ([TP-vocab] section 6 and [vLLM-1.1]
+ * "模拟 All-Reduce 聚合" emulate it the same way):
+ *
+ *   out[e] = partials[0][e] + partials[1][e] + ... + partials[n_parts-1][e]
+ *
+ * added in rank order in fp32 and rounded once to `dt` (round to nearest,
+ * ties to even).  With masked partials exactly one term per row is non-zero,
+ * so the sum is the owner's row bit for bit (tables without -0.0 entries).
+ *
+ * partials  HOST array of n_parts device pointers, each [n_elems] of `dt`.
+ * out       device, [n_elems] of `dt`; may be exactly equal to one of the
+ *           partials (in-place sum), must not partially overlap any.
+ * n_elems == 0 is a no-op.
+ * Errors: VPE_ERR_NULL, VPE_ERR_SHAPE (n_parts outside [1, VPE_MAX_PARTS],
+ * n_elems < 0), VPE_ERR_DTYPE, VPE_ERR_ALIGN.
+ */
+vpe_status vpe_sum_partials(const void *const *partials, int32_t n_parts, int64_t n_elems,
+                            vpe_dtype dt, void *out, void *stream);
+
+/*
+ * Prefill last-position select before the LM head ([Guide-3.3] section 6,
+ * ParallelLMHead.forward; [TP-vocab] section 4):
+ *
+ *   out[s, :] = hidden[cu_seqlens[s + 1] - 1, :]   for s in [0, n_seqs)
+ *
+ * hidden      device, [n_tokens, dim] of `dt` (all packed sequences).
+ * cu_seqlens  device, int32 [n_seqs + 1]: 0, then cumulative sequence lengths.
+ * out         device, [n_seqs, dim] of `dt`.
+ * Precondition: cu_seqlens starts at 0, rises strictly and ends at n_tokens.
+ * A row whose index cu_seqlens[s+1]-1 falls outside [0, n_tokens) is written
+ * as zeros and nothing is read for it (no out-of-bounds access).
+ * n_seqs == 0 is a no-op.
+ * Errors: VPE_ERR_NULL, VPE_ERR_SHAPE (n_tokens < 0, n_seqs < 0, dim < 1,
+ * n_tokens >= 2^31), VPE_ERR_DTYPE, VPE_ERR_ALIGN.
+ */
+vpe_status vpe_last_token_select(const void *hidden, int64_t n_tokens, int64_t dim,
+                                 vpe_dtype dt, const int32_t *cu_seqlens, int64_t n_seqs,
+                                 void *out, void *stream);
+
+/*
+ * One shard's logits, F.linear with no bias ([TP-vocab] section 4,
+ * [Guide-3.3] section 6), written at the shard's column offset of the full
+ * vocabulary (the gather-and-concatenate of [TP-vocab] section 6 and
+ * [TP-math] section 5):
+ *
+ *   logits[i * ld_out + col_offset + j] = sum_k x[i, k] * weight[j, k]
+ *                                          for i < m, j < shard_rows
+ *
+ * x       device, [m, dim] of `dt` (last-position hidden states).
+ * weight  device, [shard_rows, dim] of `dt` (the same shard layout as
+ *         vpe_embed: vocabulary rows, dim contiguous).
+ * logits  device, row-major with row stride ld_out elements, of `dt`; only
+ *         columns [col_offset, col_offset + shard_rows) of rows [0, m) are
+ *         written.  For one shard alone: ld_out = shard_rows, col_offset = 0.
+ *         To concatenate tp shards: ld_out = V, col_offset = vocab_start.
+ * Products are accumulated in fp32 (order unspecified) and rounded once to
+ * `dt` (round to nearest, ties to even).
+ * m == 0 is a no-op.
+ * Errors: VPE_ERR_NULL, VPE_ERR_SHAPE (m < 0, m > 2^21, dim < 1,
+ * shard_rows < 1), VPE_ERR_RANGE (col_offset < 0 or col_offset + shard_rows > ld_out),
+ * VPE_ERR_DTYPE, VPE_ERR_ALIGN.
+ */
+vpe_status vpe_lmhead(const void *x, int64_t m, int64_t dim, const void *weight,
+                      int64_t shard_rows, vpe_dtype dt, void *logits, int64_t ld_out,
+                      int64_t col_offset, void *stream);
+
+/* Static, NUL-terminated name of a status code ("VPE_OK", ...). */
+const char *vpe_status_string(vpe_status s);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* VPE_H */

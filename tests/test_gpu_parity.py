@@ -1,0 +1,322 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle.
+
+Embedding rows, partial sums and selected rows must match bit for bit; logits
+(bf16 or fp32 inputs, fp32 accumulation) must satisfy
+|gpu - ref| <= 1e-2 + 1e-2 |ref| against the oracle's fp64 products.
+Workload-sized LM heads that the oracle cannot finish in seconds are checked
+on sampled rows, columns and single logits, each computed by the oracle.
+"""
+import json
+import os
+import sys
+
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+pytestmark = [
+    pytest.mark.gpu,
+    pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a HIP GPU"),
+]
+
+import oracle  # noqa: E402
+import workloads as wl  # noqa: E402
+import vocab_sharded_embedding_amd as vpe  # noqa: E402
+from _gpu import as_f64, assert_logits_close, dev, oracle_threads, to_dev, to_host  # noqa: E402
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+# ---------------------------------------------------------------------------
+# cached workload inputs (generation of the large tables takes seconds)
+# ---------------------------------------------------------------------------
+_cache = {}
+
+
+def _inputs(name):
+    if name in _cache:
+        return _cache[name]
+    w = wl.WORKLOADS[name]
+    d = {"w": w, "ids": wl.workload_ids(w), "hidden": wl.workload_hidden(w),
+         "cu": wl.workload_cu_seqlens(w)}
+    d["shards"] = {r: wl.shard_table(w, r) for r in w.ranks}
+    _cache.clear()  # keep at most one workload's tables in host memory
+    _cache[name] = d
+    return d
+
+
+def _lm_rows(d):
+    """The LM head's input rows on the host (prefill: last position of each sequence)."""
+    w = d["w"]
+    if w.seqs:
+        return d["hidden"][d["cu"][1:].astype(np.int64) - 1]
+    return d["hidden"]
+
+
+# ---------------------------------------------------------------------------
+# the pages' worked examples, run on the GPU
+# ---------------------------------------------------------------------------
+def test_twelve_word_demo_on_gpu():
+    with open(os.path.join(GOLDEN, "vllm11_twelve_word_demo.json")) as f:
+        g = json.load(f)
+    V, D, tp = g["vocab"], g["dim"], g["tp"]
+    ids = to_dev(np.array(g["ids"], dtype=np.int64))
+    parts = []
+    for rank in range(tp):
+        start, end = vpe.vpe_shard_range(V, tp, rank)
+        shard = (np.arange(start, end, dtype=np.float32)[:, None] * 10.0
+                 + np.arange(D, dtype=np.float32)[None, :])
+        p = vpe.vpe_embed(ids, to_dev(shard), start)
+        assert to_host(p).tolist() == g[f"rank{rank}"]["partial"]
+        parts.append(p)
+    total = vpe.vpe_sum_partials(parts)
+    torch.cuda.synchronize()
+    assert to_host(total).tolist() == g["sum"]
+
+
+def test_arange_4x2_demo_on_gpu():
+    with open(os.path.join(GOLDEN, "tpvocab_arange_4x2.json")) as f:
+        g = json.load(f)
+    full = np.arange(1, 9, dtype=np.float32).reshape(4, 2)
+    tok = to_dev(np.array(g["stated"]["tokens"], dtype=np.int32))
+    parts = []
+    for rank in range(2):
+        s, e = vpe.vpe_shard_range(4, 2, rank)
+        p = vpe.vpe_embed(tok, to_dev(full[s:e]), s)
+        assert to_host(p).tolist() == g["derived_by_hand"][f"rank{rank}_partial"]
+        parts.append(p)
+    assert to_host(vpe.vpe_sum_partials(parts)).tolist() == g["derived_by_hand"]["sum"]
+    # LM head: shard logits at their vocab offsets give the closed form
+    x = np.array([[1, 2], [-3, 5], [7, 0]], dtype=np.float32)
+    logits = torch.full((3, 4), float("nan"), device=dev())
+    for rank in range(2):
+        s, e = vpe.vpe_shard_range(4, 2, rank)
+        vpe.vpe_lmhead(to_dev(x), to_dev(full[s:e]), logits, col_offset=s)
+    a, b = x[:, 0].astype(np.float64), x[:, 1].astype(np.float64)
+    closed = np.stack([a + 2 * b, 3 * a + 4 * b, 5 * a + 6 * b, 7 * a + 8 * b], axis=1)
+    assert np.array_equal(as_f64(to_host(logits)), closed)
+
+
+# ---------------------------------------------------------------------------
+# embedding lookup at every workload, every rank it runs: bit-exact
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("name", wl.WORKLOAD_ORDER)
+def test_embed_matches_oracle(name):
+    d = _inputs(name)
+    w = d["w"]
+    ids_d = to_dev(d["ids"])
+    for rank in w.ranks:
+        _say(f"embed {name} rank {rank}: n={w.n_ids} dim={w.dim} {w.dtype}")
+        start = w.rank_start(rank)
+        out = vpe.vpe_embed(ids_d, to_dev(d["shards"][rank]), start)
+        ref = oracle.embed(d["ids"], d["shards"][rank], start, nthreads=oracle_threads())
+        got = to_host(out)
+        assert got.shape == ref.shape
+        assert got.tobytes() == ref.tobytes(), f"{name} rank {rank}: embedding differs"
+        owned = (d["ids"] >= start) & (d["ids"] < start + w.shard_rows)
+        assert np.all(got[~owned] == 0)
+
+
+@pytest.mark.parametrize("name", ["tiny_v4096_d64_f32_tp2", "qwen3_0p6b_tp2_all_ranks"])
+def test_sum_of_partials_is_full_lookup(name):
+    d = _inputs(name)
+    w = d["w"]
+    ids_d = to_dev(d["ids"])
+    parts = [vpe.vpe_embed(ids_d, to_dev(d["shards"][r]), w.rank_start(r)) for r in w.ranks]
+    total = to_host(vpe.vpe_sum_partials(parts))
+    full = np.concatenate([d["shards"][r] for r in w.ranks], axis=0)
+    ref_full = oracle.embed(d["ids"], full, 0, nthreads=oracle_threads())
+    ref_sum = oracle.sum_partials([to_host(p) for p in parts])
+    assert total.tobytes() == ref_full.tobytes()
+    assert total.tobytes() == ref_sum.tobytes()
+    assert total.tobytes() == np.take(full, d["ids"], axis=0).tobytes()
+
+
+def test_sum_in_place_and_general_values():
+    # partials that are all non-zero exercise the fp32 add order and the rounding
+    rng = np.random.default_rng(21)
+    for dtype in ("f32", "bf16"):
+        for n in (1, 7, 4096 + 5):
+            parts_h = [wl.hidden_states(30 + r, 1, n, dtype).reshape(-1) for r in range(3)]
+            parts = [to_dev(p) for p in parts_h]
+            ref = oracle.sum_partials(parts_h)
+            got = to_host(vpe.vpe_sum_partials(parts))
+            assert got.tobytes() == ref.tobytes(), (dtype, n)
+            vpe.vpe_sum_partials(parts, out=parts[0])  # in place into partial 0
+            assert to_host(parts[0]).tobytes() == ref.tobytes(), (dtype, n)
+    del rng
+
+
+# ---------------------------------------------------------------------------
+# last-position select
+# ---------------------------------------------------------------------------
+def test_select_prefill_workload():
+    d = _inputs("qwen3_0p6b_tp1_prefill")
+    out = vpe.vpe_last_token_select(to_dev(d["hidden"]), to_dev(d["cu"]))
+    ref = oracle.last_token_select(d["hidden"], d["cu"])
+    assert to_host(out).tobytes() == ref.tobytes()
+
+
+@pytest.mark.parametrize("dtype,dim", [("bf16", 1024), ("bf16", 3), ("f32", 4), ("f32", 130)])
+def test_select_ragged(dtype, dim):
+    cu = wl.cu_seqlens_ragged(40 + dim, 37, 1, 50)
+    H = wl.hidden_states(41, int(cu[-1]), dim, dtype)
+    out = vpe.vpe_last_token_select(to_dev(H), to_dev(cu))
+    assert to_host(out).tobytes() == oracle.last_token_select(H, cu).tobytes()
+
+
+def test_select_out_of_range_index_gives_zero_row():
+    H = np.arange(40, dtype=np.float32).reshape(10, 4) + 1
+    cu = np.array([0, 0, 4, 10, 12], dtype=np.int32)  # an empty first sequence; 12 > 10 tokens
+    out = to_host(vpe.vpe_last_token_select(to_dev(H), to_dev(cu)))
+    assert np.all(out[0] == 0) and np.all(out[3] == 0)
+    assert out[1].tobytes() == H[3].tobytes() and out[2].tobytes() == H[9].tobytes()
+
+
+# ---------------------------------------------------------------------------
+# LM head: small and ragged shapes, full oracle comparison
+# ---------------------------------------------------------------------------
+LM_SHAPES = [
+    # (m, n, k): tile multiples, ragged tails in every dimension, K not a multiple of 8
+    (1, 1, 8), (3, 5, 7), (16, 128, 64), (17, 129, 65), (32, 1000, 200), (64, 777, 1024),
+    (65, 300, 96), (128, 256, 128), (130, 515, 264), (257, 131, 40), (300, 2100, 1024),
+]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("m,n,k", LM_SHAPES)
+def test_lmhead_shapes(dtype, m, n, k):
+    X = wl.hidden_states(50 + m, m, k, dtype)
+    W = wl.table_rows(60 + n, n, k, dtype, 0, n, std=0.5)
+    got = to_host(vpe.vpe_lmhead(to_dev(X), to_dev(W)))
+    ref = oracle.lmhead_f64(X, W, nthreads=oracle_threads())
+    assert_logits_close(got, ref, f"lmhead {dtype} {m}x{n}x{k}")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("ld,col", [(1500, 0), (1500, 500), (1501, 3), (1003, 1)])
+def test_lmhead_writes_only_its_columns(dtype, ld, col):
+    m, n, k = 40, 1000, 128
+    X = wl.hidden_states(70, m, k, dtype)
+    W = wl.table_rows(71, n, k, dtype, 0, n, std=0.5)
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    logits = torch.full((m, ld), 12345.0, dtype=tdt, device=dev())
+    vpe.vpe_lmhead(to_dev(X), to_dev(W), logits, col_offset=col)
+    got = to_host(logits)
+    ref = oracle.lmhead_f64(X, W)
+    assert_logits_close(got[:, col:col + n], ref, f"lmhead {dtype} ld={ld} col={col}")
+    sentinel = as_f64(got)
+    assert np.all(sentinel[:, :col] == 12345.0) and np.all(sentinel[:, col + n:] == 12345.0)
+
+
+# ---------------------------------------------------------------------------
+# LM head at the workloads
+# ---------------------------------------------------------------------------
+def _lm_run(d, logits_cols, col_of):
+    w = d["w"]
+    x_h = _lm_rows(d)
+    tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    logits = torch.empty((x_h.shape[0], logits_cols), dtype=tdt, device=dev())
+    x_d = to_dev(x_h)
+    for r in w.ranks:
+        vpe.vpe_lmhead(x_d, to_dev(d["shards"][r]), logits, col_offset=col_of(r))
+    return x_h, to_host(logits)
+
+
+@pytest.mark.parametrize("name", ["tiny_v4096_d64_f32_tp2", "qwen3_0p6b_tp2_rank0",
+                                  "qwen3_0p6b_tp1_prefill"])
+def test_lmhead_workload_full(name):
+    d = _inputs(name)
+    w = d["w"]
+    _say(f"lmhead {name}: M={w.lm_rows} shard rows={w.shard_rows} dim={w.dim}")
+    if w.concat:
+        x_h, got = _lm_run(d, w.vocab, w.rank_start)
+    else:
+        x_h, got = _lm_run(d, w.shard_rows, lambda r: 0)
+    ref = np.zeros(got.shape, dtype=np.float64)
+    for r in w.ranks:
+        oracle.lmhead_f64(x_h, d["shards"][r], out=ref,
+                          col_offset=w.rank_start(r) if w.concat else 0,
+                          nthreads=oracle_threads())
+    assert_logits_close(got, ref, name)
+
+
+@pytest.mark.parametrize("name", ["qwen3_0p6b_tp2_all_ranks", "large_v151936_d4096_tp4_rank2"])
+def test_lmhead_workload_sampled(name):
+    d = _inputs(name)
+    w = d["w"]
+    _say(f"lmhead {name} (sampled): M={w.lm_rows} shard rows={w.shard_rows} dim={w.dim}")
+    if w.concat:
+        x_h, got = _lm_run(d, w.vocab, w.rank_start)
+    else:
+        x_h, got = _lm_run(d, w.shard_rows, lambda r: 0)
+    rng = np.random.default_rng(99)
+    M = x_h.shape[0]
+    nt = oracle_threads()
+    for r in w.ranks:
+        W = d["shards"][r]
+        off = w.rank_start(r) if w.concat else 0
+        # whole rows of logits (every vocabulary column of this shard)
+        for m in [0, M - 1, int(rng.integers(0, M))]:
+            ref = oracle.lmhead_f64(x_h[m:m + 1], W, nthreads=nt)
+            assert_logits_close(got[m:m + 1, off:off + w.shard_rows], ref, f"{name} row {m}")
+        # whole columns (every row of X), including the ragged last tile
+        for j in [0, w.shard_rows - 1, int(rng.integers(0, w.shard_rows))]:
+            ref = oracle.lmhead_f64(x_h, W[j:j + 1], nthreads=nt)
+            assert_logits_close(got[:, off + j:off + j + 1], ref, f"{name} col {j}")
+        # scattered single logits
+        ms = rng.integers(0, M, size=500)
+        js = rng.integers(0, w.shard_rows, size=500)
+        ref = np.array([oracle.logit_f64(x_h, W, int(a), int(b)) for a, b in zip(ms, js)])
+        assert_logits_close(got[ms, off + js], ref, f"{name} sampled")
+
+
+# ---------------------------------------------------------------------------
+# edge cases
+# ---------------------------------------------------------------------------
+def test_empty_calls_are_no_ops():
+    W = to_dev(np.ones((8, 16), np.float32))
+    out = vpe.vpe_embed(to_dev(np.zeros(0, np.int32)), W, 0)
+    assert out.shape == (0, 16)
+    logits = vpe.vpe_lmhead(to_dev(np.zeros((0, 16), np.float32)), W)
+    assert logits.shape == (0, 8)
+    sel = vpe.vpe_last_token_select(to_dev(np.zeros((0, 16), np.float32)),
+                                    to_dev(np.zeros(1, np.int32)))
+    assert sel.shape == (0, 16)
+    torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("dtype,dim", [("bf16", 1), ("bf16", 3), ("bf16", 8), ("bf16", 520),
+                                       ("f32", 1), ("f32", 2), ("f32", 6), ("f32", 300),
+                                       ("bf16", 8200)])
+@pytest.mark.parametrize("itype", [np.int32, np.int64])
+def test_embed_odd_dims_and_out_of_range_ids(dtype, dim, itype):
+    V, tp, rank = 96, 3, 1
+    start = V // tp * rank
+    shard = wl.table_rows(80, V, dim, dtype, start, start + V // tp)
+    rng = np.random.default_rng(dim)
+    ids = rng.integers(-1000, V + 1000, size=333).astype(itype)
+    ids[:4] = [start, start + V // tp - 1, start - 1, start + V // tp]
+    if itype == np.int64:
+        ids[4:6] = [-(2 ** 40), 2 ** 40 + start]  # would alias into the shard if truncated
+    got = to_host(vpe.vpe_embed(to_dev(ids), to_dev(shard), start))
+    assert got.tobytes() == oracle.embed(ids, shard, start).tobytes()
+
+
+def test_binding_rejects_bad_arguments():
+    W = to_dev(np.ones((8, 16), np.float32))
+    x = to_dev(np.ones((2, 16), np.float32))
+    with pytest.raises(vpe.VpeError) as e:
+        vpe.vpe_lmhead(x, W, torch.empty((2, 10), device=dev()), col_offset=4)
+    assert e.value.status == vpe.VPE_ERR_RANGE
+    with pytest.raises(TypeError):
+        vpe.vpe_lmhead(x.to(torch.bfloat16), W)
+    with pytest.raises(vpe.VpeError) as e:
+        vpe.vpe_shard_range(151936, 3, 0)
+    assert e.value.status == vpe.VPE_ERR_SHARD

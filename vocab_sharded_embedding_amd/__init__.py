@@ -1,0 +1,229 @@
+"""vocab_sharded_embedding_amd: the vocab-parallel embedding and LM head on MI355X.
+
+A thin Python binding over ``libvpe.so`` (C ABI declared in ``include/vpe.h``).
+Functions here only marshal arguments: they check tensor placement, dtype and
+layout, allocate outputs with ``torch.empty`` when none is given, and pass raw
+device pointers plus the current HIP stream to the library.  Every step of the
+computation runs in the library's HIP kernels; there is no fallback path, and
+loading fails loudly when the library is missing or cannot be loaded.
+
+Names follow the C ABI: ``vpe_shard_range``, ``vpe_embed``,
+``vpe_sum_partials``, ``vpe_last_token_select``, ``vpe_lmhead``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence, Tuple
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libvpe.so")
+
+VPE_OK, VPE_ERR_NULL, VPE_ERR_SHAPE, VPE_ERR_DTYPE = 0, 1, 2, 3
+VPE_ERR_ALIGN, VPE_ERR_SHARD, VPE_ERR_LAUNCH, VPE_ERR_RANGE = 4, 5, 6, 7
+VPE_F32, VPE_BF16 = 0, 1
+VPE_I32, VPE_I64 = 0, 1
+VPE_MAX_PARTS = 64
+
+EXPORTED_SYMBOLS = ("vpe_shard_range", "vpe_embed", "vpe_sum_partials",
+                    "vpe_last_token_select", "vpe_lmhead", "vpe_status_string")
+
+
+class VpeError(RuntimeError):
+    """A libvpe call returned a status other than VPE_OK."""
+
+    def __init__(self, fn: str, status: int, name: str):
+        super().__init__(f"{fn} failed: {name} ({status})")
+        self.status = status
+        self.status_name = name
+
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load libvpe.so (building it first only if no build exists)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        from . import build as _build
+        _build.build()
+    lib = ctypes.CDLL(path)
+    i64, i32, vp, ci = ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p, ctypes.c_int
+    lib.vpe_shard_range.argtypes = [i64, i32, i32, ctypes.POINTER(i64), ctypes.POINTER(i64)]
+    lib.vpe_embed.argtypes = [vp, ci, i64, vp, ci, i64, i64, i64, vp, vp]
+    lib.vpe_sum_partials.argtypes = [ctypes.POINTER(vp), i32, i64, ci, vp, vp]
+    lib.vpe_last_token_select.argtypes = [vp, i64, i64, ci, vp, i64, vp, vp]
+    lib.vpe_lmhead.argtypes = [vp, i64, i64, vp, i64, ci, vp, i64, i64, vp]
+    for name in EXPORTED_SYMBOLS[:-1]:
+        getattr(lib, name).restype = ci
+    lib.vpe_status_string.argtypes = [ci]
+    lib.vpe_status_string.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def status_name(status: int) -> str:
+    return load_library().vpe_status_string(status).decode()
+
+
+def _check(fn: str, status: int) -> None:
+    if status != VPE_OK:
+        raise VpeError(fn, status, status_name(status))
+
+
+# ---------------------------------------------------------------------------
+# tensor marshalling
+# ---------------------------------------------------------------------------
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.float32:
+        return VPE_F32
+    if t.dtype == torch.bfloat16:
+        return VPE_BF16
+    raise TypeError(f"tensor dtype must be float32 or bfloat16, got {t.dtype}")
+
+
+def _itype_code(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.int32:
+        return VPE_I32
+    if t.dtype == torch.int64:
+        return VPE_I64
+    raise TypeError(f"token ids must be int32 or int64, got {t.dtype}")
+
+
+def _need_device(name: str, t) -> None:
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a HIP device tensor, got device {t.device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _stream_handle(device) -> int:
+    torch = _torch()
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _same_device(*ts) -> None:
+    devs = {t.device for t in ts}
+    if len(devs) != 1:
+        raise ValueError(f"all tensors must be on one device, got {sorted(map(str, devs))}")
+
+
+# ---------------------------------------------------------------------------
+# the five calls
+# ---------------------------------------------------------------------------
+def vpe_shard_range(vocab: int, tp_size: int, tp_rank: int) -> Tuple[int, int]:
+    """(vocab_start, vocab_end) owned by tp_rank: contiguous V/tp rows in rank order."""
+    lib = load_library()
+    s, e = ctypes.c_int64(), ctypes.c_int64()
+    _check("vpe_shard_range", lib.vpe_shard_range(vocab, tp_size, tp_rank,
+                                                  ctypes.byref(s), ctypes.byref(e)))
+    return s.value, e.value
+
+
+def vpe_embed(ids, weight, vocab_start: int, out=None):
+    """One shard's masked lookup: ids [*] x weight [R, D] -> out [*, D].
+
+    Rows for ids outside [vocab_start, vocab_start + R) are +0.0.
+    """
+    torch = _torch()
+    _need_device("ids", ids)
+    _need_device("weight", weight)
+    if weight.dim() != 2:
+        raise ValueError("weight must be [shard_rows, dim]")
+    rows, dim = weight.shape
+    if out is None:
+        out = torch.empty((*ids.shape, dim), dtype=weight.dtype, device=weight.device)
+    _need_device("out", out)
+    if out.dtype != weight.dtype or out.numel() != ids.numel() * dim:
+        raise ValueError("out must have the weight's dtype and ids.numel() * dim elements")
+    _same_device(ids, weight, out)
+    _check("vpe_embed", load_library().vpe_embed(
+        ids.data_ptr(), _itype_code(ids), ids.numel(), weight.data_ptr(), _dtype_code(weight),
+        rows, dim, int(vocab_start), out.data_ptr(), _stream_handle(weight.device)))
+    return out
+
+
+def vpe_sum_partials(partials: Sequence, out=None):
+    """Elementwise sum of same-shape partials (rank order, fp32, one rounding)."""
+    torch = _torch()
+    parts = list(partials)
+    if not parts:
+        raise ValueError("need at least one partial")
+    for i, p in enumerate(parts):
+        _need_device(f"partials[{i}]", p)
+        if p.shape != parts[0].shape or p.dtype != parts[0].dtype:
+            raise ValueError("partials must share shape and dtype")
+    if out is None:
+        out = torch.empty_like(parts[0])
+    _need_device("out", out)
+    if out.dtype != parts[0].dtype or out.numel() != parts[0].numel():
+        raise ValueError("out must match the partials' dtype and size")
+    _same_device(out, *parts)
+    arr = (ctypes.c_void_p * len(parts))(*[p.data_ptr() for p in parts])
+    _check("vpe_sum_partials", load_library().vpe_sum_partials(
+        arr, len(parts), parts[0].numel(), _dtype_code(parts[0]), out.data_ptr(),
+        _stream_handle(out.device)))
+    return out
+
+
+def vpe_last_token_select(hidden, cu_seqlens, out=None):
+    """hidden [T, D], cu_seqlens int32 [S+1] -> out [S, D] = hidden[cu[1:] - 1]."""
+    torch = _torch()
+    _need_device("hidden", hidden)
+    _need_device("cu_seqlens", cu_seqlens)
+    if hidden.dim() != 2:
+        raise ValueError("hidden must be [n_tokens, dim]")
+    if cu_seqlens.dtype != torch.int32 or cu_seqlens.dim() != 1 or cu_seqlens.numel() < 1:
+        raise ValueError("cu_seqlens must be a 1-D int32 tensor with at least one entry")
+    t, d = hidden.shape
+    s = cu_seqlens.numel() - 1
+    if out is None:
+        out = torch.empty((s, d), dtype=hidden.dtype, device=hidden.device)
+    _need_device("out", out)
+    if out.dtype != hidden.dtype or out.numel() != s * d:
+        raise ValueError("out must be [n_seqs, dim] of hidden's dtype")
+    _same_device(hidden, cu_seqlens, out)
+    _check("vpe_last_token_select", load_library().vpe_last_token_select(
+        hidden.data_ptr(), t, d, _dtype_code(hidden), cu_seqlens.data_ptr(), s,
+        out.data_ptr(), _stream_handle(hidden.device)))
+    return out
+
+
+def vpe_lmhead(x, weight, logits=None, col_offset: int = 0):
+    """Shard logits x [M, D] . weight[R, D]^T into columns [col_offset, +R) of logits [M, ld]."""
+    torch = _torch()
+    _need_device("x", x)
+    _need_device("weight", weight)
+    if x.dim() != 2 or weight.dim() != 2 or x.shape[1] != weight.shape[1]:
+        raise ValueError("x must be [m, dim] and weight [shard_rows, dim]")
+    if x.dtype != weight.dtype:
+        raise TypeError("x and weight must share a dtype")
+    m, d = x.shape
+    rows = weight.shape[0]
+    if logits is None:
+        logits = torch.empty((m, col_offset + rows), dtype=x.dtype, device=x.device)
+    _need_device("logits", logits)
+    if logits.dim() != 2 or logits.shape[0] != m or logits.dtype != x.dtype:
+        raise ValueError("logits must be [m, ld] of x's dtype")
+    _same_device(x, weight, logits)
+    _check("vpe_lmhead", load_library().vpe_lmhead(
+        x.data_ptr(), m, d, weight.data_ptr(), rows, _dtype_code(x), logits.data_ptr(),
+        logits.shape[1], int(col_offset), _stream_handle(x.device)))
+    return logits
+
+
+from .layers import ParallelLMHead, VocabParallelEmbedding  # noqa: E402
+
+__all__ = [
+    "vpe_shard_range", "vpe_embed", "vpe_sum_partials", "vpe_last_token_select", "vpe_lmhead",
+    "VocabParallelEmbedding", "ParallelLMHead", "VpeError", "load_library", "LIB_PATH",
+]

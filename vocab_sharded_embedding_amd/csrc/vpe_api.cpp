@@ -1,0 +1,126 @@
+// The C ABI of libvpe.so: argument validation and dispatch to the kernel
+// launchers.  Plain C++ with no HIP headers: everything here runs on the host
+// before any HIP call, so every rejected call enqueues nothing.  The exported
+// entry points and their contracts are declared in include/vpe.h.
+#include "../../include/vpe.h"
+
+#include <stdint.h>
+
+#include "vpe_launch.h"
+
+namespace {
+
+bool known_dtype(vpe_dtype dt) { return dt == VPE_F32 || dt == VPE_BF16; }
+bool known_itype(vpe_itype it) { return it == VPE_I32 || it == VPE_I64; }
+int64_t dtype_bytes(vpe_dtype dt) { return dt == VPE_F32 ? 4 : 2; }
+int64_t itype_bytes(vpe_itype it) { return it == VPE_I32 ? 4 : 8; }
+
+bool aligned(const void *p, int64_t bytes) {
+  return (reinterpret_cast<uintptr_t>(p) % static_cast<uintptr_t>(bytes)) == 0;
+}
+
+vpe_status launched(int rc) { return rc == 0 ? VPE_OK : VPE_ERR_LAUNCH; }
+
+// Largest element count any single tensor may have (far above what one
+// device holds): indexes inside the kernels are 64-bit and every grid stays
+// below 2^32 work-items per dimension at this size.
+constexpr int64_t kMaxElems = int64_t(1) << 39;
+
+}  // namespace
+
+extern "C" {
+
+vpe_status vpe_shard_range(int64_t vocab, int32_t tp_size, int32_t tp_rank,
+                           int64_t *vocab_start, int64_t *vocab_end) {
+  if (!vocab_start || !vocab_end) return VPE_ERR_NULL;
+  if (vocab < 1 || tp_size < 1 || tp_rank < 0 || tp_rank >= tp_size) return VPE_ERR_SHARD;
+  if (vocab % tp_size != 0) return VPE_ERR_SHARD;
+  const int64_t rows = vocab / tp_size;
+  *vocab_start = rows * tp_rank;
+  *vocab_end = *vocab_start + rows;
+  return VPE_OK;
+}
+
+vpe_status vpe_embed(const void *ids, vpe_itype itype, int64_t n, const void *weight,
+                     vpe_dtype dt, int64_t shard_rows, int64_t dim, int64_t vocab_start,
+                     void *out, void *stream) {
+  if (!known_dtype(dt) || !known_itype(itype)) return VPE_ERR_DTYPE;
+  if (n < 0 || dim < 1 || shard_rows < 1) return VPE_ERR_SHAPE;
+  if (n > kMaxElems / dim || shard_rows > kMaxElems / dim) return VPE_ERR_SHAPE;
+  if (n == 0) return VPE_OK;
+  if (!ids || !weight || !out) return VPE_ERR_NULL;
+  if (!aligned(ids, itype_bytes(itype)) || !aligned(weight, dtype_bytes(dt)) ||
+      !aligned(out, dtype_bytes(dt)))
+    return VPE_ERR_ALIGN;
+  return launched(vpe::launch_embed(ids, itype == VPE_I32 ? 0 : 1, n, weight, shard_rows,
+                                    dim * dtype_bytes(dt), vocab_start, out, stream));
+}
+
+vpe_status vpe_sum_partials(const void *const *partials, int32_t n_parts, int64_t n_elems,
+                            vpe_dtype dt, void *out, void *stream) {
+  if (!known_dtype(dt)) return VPE_ERR_DTYPE;
+  if (n_parts < 1 || n_parts > VPE_MAX_PARTS || n_elems < 0 || n_elems > kMaxElems)
+    return VPE_ERR_SHAPE;
+  if (n_elems == 0) return VPE_OK;
+  if (!partials || !out) return VPE_ERR_NULL;
+  for (int32_t r = 0; r < n_parts; ++r) {
+    if (!partials[r]) return VPE_ERR_NULL;
+    if (!aligned(partials[r], dtype_bytes(dt))) return VPE_ERR_ALIGN;
+  }
+  if (!aligned(out, dtype_bytes(dt))) return VPE_ERR_ALIGN;
+  return launched(vpe::launch_sum_partials(partials, n_parts, n_elems, dt == VPE_BF16 ? 1 : 0,
+                                           out, stream));
+}
+
+vpe_status vpe_last_token_select(const void *hidden, int64_t n_tokens, int64_t dim,
+                                 vpe_dtype dt, const int32_t *cu_seqlens, int64_t n_seqs,
+                                 void *out, void *stream) {
+  if (!known_dtype(dt)) return VPE_ERR_DTYPE;
+  if (n_tokens < 0 || n_seqs < 0 || dim < 1) return VPE_ERR_SHAPE;
+  // cu_seqlens holds int32 positions, so the token count must fit in int32
+  if (n_tokens > INT32_MAX || n_tokens > kMaxElems / dim || n_seqs > kMaxElems / dim)
+    return VPE_ERR_SHAPE;
+  if (n_seqs == 0) return VPE_OK;
+  if (!hidden || !cu_seqlens || !out) return VPE_ERR_NULL;
+  if (!aligned(hidden, dtype_bytes(dt)) || !aligned(out, dtype_bytes(dt)) ||
+      !aligned(cu_seqlens, 4))
+    return VPE_ERR_ALIGN;
+  return launched(vpe::launch_last_token_select(hidden, n_tokens, dim * dtype_bytes(dt),
+                                                cu_seqlens, n_seqs, out, stream));
+}
+
+vpe_status vpe_lmhead(const void *x, int64_t m, int64_t dim, const void *weight,
+                      int64_t shard_rows, vpe_dtype dt, void *logits, int64_t ld_out,
+                      int64_t col_offset, void *stream) {
+  if (!known_dtype(dt)) return VPE_ERR_DTYPE;
+  if (m < 0 || dim < 1 || shard_rows < 1) return VPE_ERR_SHAPE;
+  if (m > kMaxElems / dim || shard_rows > kMaxElems / dim) return VPE_ERR_SHAPE;
+  // the grid's second dimension counts blocks of at least 64 rows of X and
+  // must stay below 65536
+  if (m > (int64_t(1) << 21)) return VPE_ERR_SHAPE;
+  if (col_offset < 0 || ld_out < 1 || shard_rows > ld_out - col_offset) return VPE_ERR_RANGE;
+  if (m > kMaxElems / ld_out) return VPE_ERR_SHAPE;
+  if (m == 0) return VPE_OK;
+  if (!x || !weight || !logits) return VPE_ERR_NULL;
+  if (!aligned(x, dtype_bytes(dt)) || !aligned(weight, dtype_bytes(dt)) ||
+      !aligned(logits, dtype_bytes(dt)))
+    return VPE_ERR_ALIGN;
+  return launched(vpe::launch_lmhead(x, m, dim, weight, shard_rows, dt == VPE_BF16 ? 1 : 0,
+                                     logits, ld_out, col_offset, stream));
+}
+
+const char *vpe_status_string(vpe_status s) {
+  switch (s) {
+    case VPE_OK: return "VPE_OK";
+    case VPE_ERR_NULL: return "VPE_ERR_NULL";
+    case VPE_ERR_SHAPE: return "VPE_ERR_SHAPE";
+    case VPE_ERR_DTYPE: return "VPE_ERR_DTYPE";
+    case VPE_ERR_ALIGN: return "VPE_ERR_ALIGN";
+    case VPE_ERR_SHARD: return "VPE_ERR_SHARD";
+    case VPE_ERR_LAUNCH: return "VPE_ERR_LAUNCH";
+    case VPE_ERR_RANGE: return "VPE_ERR_RANGE";
+  }
+  return "VPE_ERR_UNKNOWN";
+}
+
+}  // extern "C"

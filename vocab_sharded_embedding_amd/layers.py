@@ -1,0 +1,77 @@
+"""Page-shaped layer objects over the C ABI (argument marshalling only).
+
+``VocabParallelEmbedding`` and ``ParallelLMHead`` keep the constructor and
+``weight_loader`` of the nano-vllm layers the pages walk through
+(devpress.csdn.net/amd/6a3de260... sections 3-4; blog.xiaohansong.com
+"从零实现 vLLM (1.1)" source analysis; AIInfraGuide 3.3 section 6): a rank
+holds rows [vocab_start, vocab_end) of the [V, D] table as a [V/tp, D]
+parameter.  Their ``forward`` calls the library; there is no collective here:
+ranks emulated in one process combine their outputs with
+``VocabParallelEmbedding.sum_partials`` (the embedding's all-reduce) and by
+writing their logits at ``vocab_start`` into one [M, V] buffer (the LM head's
+gather and concatenation).
+"""
+from __future__ import annotations
+
+from typing import Optional, Sequence
+
+import torch
+
+from . import vpe_embed, vpe_last_token_select, vpe_lmhead, vpe_shard_range, vpe_sum_partials
+
+
+class VocabParallelEmbedding(torch.nn.Module):
+    def __init__(self, num_embeddings: int, embedding_dim: int, tp_size: int = 1,
+                 tp_rank: int = 0, dtype: torch.dtype = torch.bfloat16,
+                 device: Optional[torch.device] = None):
+        super().__init__()
+        self.num_embeddings = num_embeddings
+        self.embedding_dim = embedding_dim
+        self.tp_size = tp_size
+        self.tp_rank = tp_rank
+        self.vocab_start_idx, self.vocab_end_idx = vpe_shard_range(num_embeddings, tp_size,
+                                                                   tp_rank)
+        self.num_embeddings_per_partition = self.vocab_end_idx - self.vocab_start_idx
+        self.weight = torch.nn.Parameter(
+            torch.empty(self.num_embeddings_per_partition, embedding_dim, dtype=dtype,
+                        device=device),
+            requires_grad=False)
+        self.weight.weight_loader = self.weight_loader
+
+    def weight_loader(self, param: torch.nn.Parameter, loaded_weight: torch.Tensor) -> None:
+        """Copy this rank's rows of the full [V, D] table into the shard (setup only)."""
+        shard = param.data.size(0)
+        piece = loaded_weight.narrow(0, self.tp_rank * shard, shard)
+        if piece.shape != param.data.shape:
+            raise ValueError(f"loaded table slice {tuple(piece.shape)} does not match "
+                             f"shard {tuple(param.data.shape)}")
+        param.data.copy_(piece)
+
+    def forward(self, ids: torch.Tensor, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+        """This rank's partial embedding (zero rows for ids it does not own)."""
+        return vpe_embed(ids, self.weight, self.vocab_start_idx, out=out)
+
+    @staticmethod
+    def sum_partials(partials: Sequence[torch.Tensor],
+                     out: Optional[torch.Tensor] = None) -> torch.Tensor:
+        """The ranks' partials summed on one device (the all-reduce of the embedding)."""
+        return vpe_sum_partials(partials, out=out)
+
+
+class ParallelLMHead(VocabParallelEmbedding):
+    def forward(self, hidden: torch.Tensor, cu_seqlens: Optional[torch.Tensor] = None,
+                logits: Optional[torch.Tensor] = None) -> torch.Tensor:
+        """This rank's logits.
+
+        With ``cu_seqlens`` (prefill) only the last position of every sequence
+        is projected.  ``logits`` may be this rank's [M, V/tp] buffer or the
+        full [M, V] buffer, in which case the shard lands at its vocab_start.
+        """
+        x = hidden if cu_seqlens is None else vpe_last_token_select(hidden, cu_seqlens)
+        if logits is None:
+            return vpe_lmhead(x, self.weight)
+        if logits.shape[1] == self.num_embeddings_per_partition:
+            return vpe_lmhead(x, self.weight, logits, col_offset=0)
+        if logits.shape[1] == self.num_embeddings:
+            return vpe_lmhead(x, self.weight, logits, col_offset=self.vocab_start_idx)
+        raise ValueError("logits must be [M, V/tp] (one shard) or [M, V] (all shards)")
