@@ -1,0 +1,306 @@
+#!/usr/bin/env python3
+"""Benchmark of the vocab-parallel hot path on one MI355X.
+
+A step is one pass of the whole path over one batch of the workload: every
+emulated rank's masked embedding lookup, the on-device sum of the partials
+(when several ranks run), the prefill last-position select (prefill
+workloads), and every rank's LM-head logits written at its column offset.
+
+Default workload: Qwen3-0.6B tp=2 rank-0 shard (table rows [0, 75968) of
+151936 x 1024 bf16; 8192 uniform ids; LM head over 256 hidden rows ->
+[256, 75968] logits).  Inputs are synthetic (seeded, see workloads.py) and
+resident in HBM before timing starts.  Several copies of every input and
+output are allocated and steps rotate through them, so that a step does not
+find the previous step's table in the 256 MB Infinity Cache.
+
+Prints ONE JSON line.  Kernel durations come from HIP events recorded on
+the launch stream around every kernel inside the timed region; the roofline
+entry is for the dominant kernel (most algorithmic bytes).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "embed rows/s + GB/s; LM-head logits GB/s (decode) & TFLOP/s (batch); %roofline"
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, AMD published
+BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix, AMD published
+FP32_VECTOR_PEAK_TFLOPS = 157.3
+DEFAULT_WORKLOAD = "qwen3_0p6b_tp2_rank0"
+CACHE_DEFEAT_BYTES = 1 << 30  # rotate through at least this many bytes of inputs
+
+
+def parse_args():
+    p = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=200)
+    p.add_argument("--warmup", type=int, default=20)
+    p.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    p.add_argument("--copies", type=int, default=0,
+                   help="input copies to rotate through (0 = enough for >= 1 GiB)")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-threads", type=int, default=0, help="0 = min(16, cores available)")
+    return p.parse_args()
+
+
+def algorithmic_bytes(w, ids, ranks_owned):
+    """Bytes the method must move per step, by kernel kind."""
+    s = w.elem_bytes
+    D = w.dim
+    idb = ids.dtype.itemsize
+    out = {}
+    n = ids.size
+    # embed per rank: read ids, write every output row, read only owned rows
+    out["embed"] = [n * idb + n * D * s + h * D * s for h in ranks_owned]
+    if len(w.ranks) > 1:
+        out["sum"] = [(len(w.ranks) + 1) * n * D * s]
+    if w.seqs:
+        out["select"] = [w.seqs * (4 + 2 * D * s)]
+    M = w.lm_rows
+    R = w.shard_rows
+    out["lmhead"] = [M * D * s + R * D * s + M * R * s for _ in w.ranks]
+    flops = {"lmhead": [2 * M * R * D for _ in w.ranks]}
+    return out, flops
+
+
+def main():
+    args = parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
+              "(tensor-parallel ranks are emulated on one device)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import vocab_sharded_embedding_amd as vpe
+    import workloads as wl
+
+    if not torch.cuda.is_available():
+        print("bench.py: no HIP device visible", file=sys.stderr)
+        sys.exit(2)
+    if args.workload not in wl.WORKLOADS:
+        print(f"bench.py: unknown workload {args.workload}; choose from {wl.WORKLOAD_ORDER}",
+              file=sys.stderr)
+        sys.exit(2)
+    w = wl.WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    lib = vpe.load_library()
+    tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    s = w.elem_bytes
+
+    def up(a):
+        a = np.ascontiguousarray(a)
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
+        return torch.from_numpy(a).to(dev)
+
+    # ---------------- inputs (host, seeded) ----------------
+    t0 = time.time()
+    ids_h = wl.workload_ids(w)
+    hidden_h = wl.workload_hidden(w)
+    cu_h = wl.workload_cu_seqlens(w)
+    shards_h = {r: wl.shard_table(w, r) for r in w.ranks}
+    gen_s = time.time() - t0
+    owned = [int(np.count_nonzero((ids_h >= w.rank_start(r)) &
+                                  (ids_h < w.rank_start(r) + w.shard_rows))) for r in w.ranks]
+
+    # ---------------- device copies ----------------
+    M = w.lm_rows
+    per_copy = (sum(a.nbytes for a in shards_h.values()) + ids_h.nbytes + hidden_h.nbytes
+                + len(w.ranks) * ids_h.size * w.dim * s
+                + M * (w.vocab if w.concat else w.shard_rows) * s)
+    copies = args.copies or max(1, -(-CACHE_DEFEAT_BYTES // per_copy))
+    base = {"ids": up(ids_h), "hidden": up(hidden_h),
+            "cu": up(cu_h) if cu_h is not None else None,
+            "shards": {r: up(a) for r, a in shards_h.items()}}
+    del shards_h
+    sets = []
+    for c in range(copies):
+        d = {k: (v.clone() if torch.is_tensor(v) else v) for k, v in base.items() if k != "shards"}
+        d["shards"] = {r: t.clone() for r, t in base["shards"].items()}
+        d["partials"] = [torch.empty((ids_h.size, w.dim), dtype=tdt, device=dev)
+                         for _ in w.ranks]
+        d["embed_out"] = (torch.empty((ids_h.size, w.dim), dtype=tdt, device=dev)
+                          if len(w.ranks) > 1 else d["partials"][0])
+        d["x"] = (torch.empty((w.seqs, w.dim), dtype=tdt, device=dev) if w.seqs
+                  else d["hidden"])
+        d["logits"] = torch.empty((M, w.vocab if w.concat else w.shard_rows), dtype=tdt,
+                                  device=dev)
+        sets.append(d)
+    del base
+    torch.cuda.synchronize()
+
+    # ---------------- C-ABI argument tuples, marshalled once ----------------
+    dcode = vpe.VPE_BF16 if w.dtype == "bf16" else vpe.VPE_F32
+    icode = vpe.VPE_I32 if ids_h.dtype == np.int32 else vpe.VPE_I64
+    import ctypes
+
+    stream = torch.cuda.current_stream(dev)
+    sh = stream.cuda_stream
+    calls = []  # per copy: list of (kind, fn, args)
+    for d in sets:
+        seq = []
+        for i, r in enumerate(w.ranks):
+            seq.append(("embed", lib.vpe_embed,
+                        (d["ids"].data_ptr(), icode, ids_h.size, d["shards"][r].data_ptr(), dcode,
+                         w.shard_rows, w.dim, w.rank_start(r), d["partials"][i].data_ptr(), sh)))
+        if len(w.ranks) > 1:
+            arr = (ctypes.c_void_p * len(w.ranks))(*[p.data_ptr() for p in d["partials"]])
+            d["_arr"] = arr
+            seq.append(("sum", lib.vpe_sum_partials,
+                        (arr, len(w.ranks), ids_h.size * w.dim, dcode, d["embed_out"].data_ptr(),
+                         sh)))
+        if w.seqs:
+            seq.append(("select", lib.vpe_last_token_select,
+                        (d["hidden"].data_ptr(), hidden_h.shape[0], w.dim, dcode,
+                         d["cu"].data_ptr(), w.seqs, d["x"].data_ptr(), sh)))
+        for r in w.ranks:
+            seq.append(("lmhead", lib.vpe_lmhead,
+                        (d["x"].data_ptr(), M, w.dim, d["shards"][r].data_ptr(), w.shard_rows,
+                         dcode, d["logits"].data_ptr(), d["logits"].shape[1],
+                         w.rank_start(r) if w.concat else 0, sh)))
+        calls.append(seq)
+
+    def run_step(k, events=None):
+        for j, (kind, fn, a) in enumerate(calls[k % copies]):
+            if events is not None:
+                events[j][0].record(stream)
+            rc = fn(*a)
+            if events is not None:
+                events[j][1].record(stream)
+            if rc != 0:
+                raise RuntimeError(f"{kind} failed: {vpe.status_name(rc)}")
+
+    with torch.cuda.stream(stream):
+        for k in range(args.warmup):
+            run_step(k)
+        torch.cuda.synchronize()
+        n_calls = len(calls[0])
+        evs = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                for _ in range(n_calls)] for _ in range(args.steps)]
+        torch.cuda.synchronize()
+        t_start = time.perf_counter()
+        for k in range(args.steps):
+            run_step(k, evs[k])
+        torch.cuda.synchronize()
+        t_total = time.perf_counter() - t_start
+
+    kinds = [c[0] for c in calls[0]]
+    per_kind_ms = {}
+    for j, kind in enumerate(kinds):
+        ms = [evs[k][j][0].elapsed_time(evs[k][j][1]) for k in range(args.steps)]
+        per_kind_ms.setdefault(kind, []).append(float(np.mean(ms)))
+
+    bytes_, flops_ = algorithmic_bytes(w, ids_h, owned)
+    step_bytes = sum(sum(v) for v in bytes_.values())
+    ms_per_step = t_total * 1e3 / args.steps
+    value = step_bytes / (ms_per_step * 1e-3) / 1e9
+
+    breakdown = {}
+    for kind, lst in per_kind_ms.items():
+        us = [m * 1e3 for m in lst]
+        b = bytes_[kind]
+        gbs = [bb / (u * 1e-6) / 1e9 for bb, u in zip(b, us)]
+        e = {"us_per_launch": [round(u, 2) for u in us], "launches_per_step": len(us),
+             "GB_per_s": [round(g, 1) for g in gbs],
+             "hbm_frac": [round(g / HBM_PEAK_GBS, 4) for g in gbs]}
+        if kind == "embed":
+            e["rows_per_s"] = [round(ids_h.size / (u * 1e-6), 1) for u in us]
+        if kind == "lmhead":
+            f = flops_["lmhead"]
+            tf = [ff / (u * 1e-6) / 1e12 for ff, u in zip(f, us)]
+            e["TFLOP_per_s"] = [round(t, 2) for t in tf]
+            peak = BF16_MFMA_PEAK_TFLOPS if w.dtype == "bf16" else FP32_VECTOR_PEAK_TFLOPS
+            e["mfma_frac" if w.dtype == "bf16" else "fp32_frac"] = [round(t / peak, 4) for t in tf]
+        breakdown[kind] = e
+
+    # dominant kernel: most algorithmic bytes per step
+    dom = max(per_kind_ms, key=lambda k: sum(bytes_[k]))
+    dom_us = float(np.mean(per_kind_ms[dom])) * 1e3
+    dom_bytes = float(np.mean(bytes_[dom]))
+    dom_flops = float(np.mean(flops_.get(dom, [0])))
+    ai = dom_flops / dom_bytes if dom_bytes else 0.0
+    ridge = (BF16_MFMA_PEAK_TFLOPS * 1e12) / (HBM_PEAK_GBS * 1e9)
+    if dom == "lmhead" and ai > ridge:
+        ach = dom_flops / (dom_us * 1e-6) / 1e12
+        roof = {"kernel": dom, "bound": "mfma", "achieved": round(ach, 2),
+                "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(ach / BF16_MFMA_PEAK_TFLOPS, 4), "traffic": None,
+                "algorithmic_flops_per_launch": dom_flops}
+    else:
+        ach = dom_bytes / (dom_us * 1e-6) / 1e9
+        roof = {"kernel": dom, "bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": None,
+                "algorithmic_bytes_per_launch": dom_bytes}
+    roof["avg_launch_us"] = round(dom_us, 3)
+
+    # ---------------- CPU baseline: the oracle on the same workload ----------------
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(w, ids_h, hidden_h, cu_h, step_bytes, args.cpu_threads)
+
+    line = {
+        "metric": METRIC, "value": round(value, 2), "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": w.dtype, "data": "synthetic",
+        "config": {"workload": w.name, "vocab": w.vocab, "dim": w.dim, "tp": w.tp,
+                   "ranks": list(w.ranks), "n_ids": int(ids_h.size), "id_dist": w.id_dist,
+                   "lm_rows": M, "seqs": w.seqs, "concat": w.concat, "rotating_copies": copies,
+                   "step_algorithmic_bytes": step_bytes},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "breakdown": breakdown,
+        "device": torch.cuda.get_device_name(dev),
+        "input_gen_s": round(gen_s, 2),
+    }
+    print(json.dumps(line), flush=True)
+
+
+def cpu_baseline(w, ids_h, hidden_h, cu_h, step_bytes, threads):
+    """The oracle, as it stands, on the same step (bounded: one pass)."""
+    import numpy as np
+
+    import oracle
+    import workloads as wl
+
+    nt = threads or max(1, min(16, len(os.sched_getaffinity(0))))
+    shards = {r: wl.shard_table(w, r) for r in w.ranks}
+    x = hidden_h
+    t0 = time.perf_counter()
+    parts = [oracle.embed(ids_h, shards[r], w.rank_start(r), nthreads=nt) for r in w.ranks]
+    if len(parts) > 1:
+        oracle.sum_partials(parts)
+    if w.seqs:
+        x = oracle.last_token_select(hidden_h, cu_h)
+    # LM head: bounded sample of rows when the full product would take too long
+    M = x.shape[0]
+    flops_full = 2.0 * M * w.shard_rows * w.dim * len(w.ranks)
+    budget_flops = 6e10  # about 30 s of single-thread fp64 loops
+    m_s = max(1, min(M, int(M * budget_flops / flops_full)))
+    for r in w.ranks:
+        oracle.lmhead_f64(x[:m_s], shards[r], nthreads=nt)
+    t = time.perf_counter() - t0
+    frac = m_s / M
+    # scale the LM-head part of the step's bytes to the sample taken
+    s = w.elem_bytes
+    lm_full = sum(M * w.dim * s + w.shard_rows * w.dim * s + M * w.shard_rows * s
+                  for _ in w.ranks)
+    sample_bytes = step_bytes - lm_full + sum(m_s * w.dim * s + w.shard_rows * w.dim * s +
+                                              m_s * w.shard_rows * s for _ in w.ranks)
+    return {"value": round(sample_bytes / t / 1e9, 3), "unit": "GB/s", "cores": nt,
+            "kind": "oracle",
+            "sample": f"whole step except LM head on {m_s} of {M} rows; {t:.2f} s wall",
+            "seconds": round(t, 3)}
+
+
+if __name__ == "__main__":
+    main()

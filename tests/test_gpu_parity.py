@@ -138,6 +138,22 @@ def test_sum_of_partials_is_full_lookup(name):
     assert total.tobytes() == np.take(full, d["ids"], axis=0).tobytes()
 
 
+def test_sum_with_negative_zero_entry_follows_the_oracle():
+    # (+0) + (-0) = +0: a -0.0 table entry is the one case where the sum of
+    # masked partials differs (in sign only) from the full lookup
+    V, D = 64, 16
+    full = wl.table_rows(90, V, D, "bf16", 0, V)
+    full[40, 3] = 0x8000
+    ids = np.arange(V, dtype=np.int32)
+    ids_d = to_dev(ids)
+    parts = [vpe.vpe_embed(ids_d, to_dev(full[r * 32:(r + 1) * 32]), r * 32) for r in range(2)]
+    got = to_host(vpe.vpe_sum_partials(parts))
+    assert got.tobytes() == oracle.sum_partials([to_host(p) for p in parts]).tobytes()
+    assert got[40, 3] == 0 and full[40, 3] == 0x8000
+    got[40, 3] = 0x8000
+    assert got.tobytes() == full.tobytes()
+
+
 def test_sum_in_place_and_general_values():
     # partials that are all non-zero exercise the fp32 add order and the rounding
     rng = np.random.default_rng(21)
@@ -206,13 +222,13 @@ def test_lmhead_writes_only_its_columns(dtype, ld, col):
     X = wl.hidden_states(70, m, k, dtype)
     W = wl.table_rows(71, n, k, dtype, 0, n, std=0.5)
     tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
-    logits = torch.full((m, ld), 12345.0, dtype=tdt, device=dev())
+    logits = torch.full((m, ld), -1536.0, dtype=tdt, device=dev())  # exact in bf16
     vpe.vpe_lmhead(to_dev(X), to_dev(W), logits, col_offset=col)
     got = to_host(logits)
     ref = oracle.lmhead_f64(X, W)
     assert_logits_close(got[:, col:col + n], ref, f"lmhead {dtype} ld={ld} col={col}")
     sentinel = as_f64(got)
-    assert np.all(sentinel[:, :col] == 12345.0) and np.all(sentinel[:, col + n:] == 12345.0)
+    assert np.all(sentinel[:, :col] == -1536.0) and np.all(sentinel[:, col + n:] == -1536.0)
 
 
 # ---------------------------------------------------------------------------

@@ -56,3 +56,11 @@ def test_workload_table_matches_page_shapes():
     assert (w.vocab, w.dim, w.shard_rows, w.rank_start(0)) == (151936, 1024, 75968, 0)
     w5 = wl.WORKLOADS["large_v151936_d4096_tp4_rank2"]
     assert (w5.shard_rows, w5.rank_start(2)) == (37984, 75968)
+
+
+def test_tables_hold_no_negative_zero():
+    w = wl.WORKLOADS["qwen3_0p6b_tp2_all_ranks"]
+    t = wl.table_rows(wl.table_seed(w), w.vocab, w.dim, "bf16", 0, 8192)
+    assert not np.any(t == 0x8000)
+    f = wl.table_rows(5, 40000, 64, "f32", 0, 40000)
+    assert not np.any(np.signbit(f) & (f == 0))

@@ -154,6 +154,11 @@ def table_rows(seed: int, vocab: int, dim: int, dtype: str, lo: int, hi: int,
 
     Returns float32 [hi-lo, dim] for "f32", uint16 bf16 bits for "bf16".
     The result does not depend on which slice is requested.
+
+    A float32 normal draw is exactly +-0 with probability about 2**-23, so a
+    Qwen3-sized table holds a few dozen zeros.  Their sign is cleared: tables
+    hold no -0.0, the condition under which the sum of masked partials equals
+    the full lookup bit for bit ((+0) + (-0) is +0).
     """
     if not (0 <= lo <= hi <= vocab):
         raise ValueError(f"bad row range [{lo},{hi}) for vocab {vocab}")
@@ -167,6 +172,10 @@ def table_rows(seed: int, vocab: int, dim: int, dtype: str, lo: int, hi: int,
         blk = rng.standard_normal((r1 - r0, dim), dtype=np.float32) * np.float32(std)
         s0, s1 = max(lo, r0), min(hi, r1)
         out[s0 - lo:s1 - lo] = _encode(blk[s0 - r0:s1 - r0], dtype)
+    if dtype == "bf16":
+        out[out == 0x8000] = 0
+    else:
+        out[out == 0] = 0.0  # -0.0 == 0 compares true: every zero becomes +0.0
     return out
 
 
