@@ -51,56 +51,116 @@ __device__ __forceinline__ int lds_piece_offset(int row, int piece) {
   return row * BK + ((piece ^ (row & 7)) << 3);  // in bf16 elements
 }
 
-// Copy a rows x BK slice (rows [r0, r0+ROWS) of a [nrows, K] matrix, columns
-// [k0, k0+BK)) into LDS.  Out-of-range rows and columns are filled with zero.
-// VEC: rows are 16-byte aligned and K % 8 == 0, so each piece is one load.
-template <int ROWS, bool VEC>
-__device__ __forceinline__ void stage_tile(uint16_t *__restrict__ lds,
-                                           const uint16_t *__restrict__ g, int64_t r0,
-                                           int64_t nrows, int64_t K, int64_t k0) {
-  constexpr int kTotal = ROWS * kPieces;
-#pragma unroll
-  for (int c = threadIdx.x; c < kTotal; c += kBlock) {
-    const int row = c / kPieces;
-    const int piece = c % kPieces;
-    const int64_t grow = r0 + row;
-    const int64_t gk = k0 + piece * 8;
-    u32x4 v = u32x4(0);
-    if (grow < nrows) {
-      const uint16_t *p = g + grow * K + gk;
-      if (VEC) {
-        if (gk < K) v = *reinterpret_cast<const u32x4 *>(p);
-      } else {
-        uint16_t e[8];
-#pragma unroll
-        for (int q = 0; q < 8; ++q) e[q] = (gk + q < K) ? p[q] : uint16_t(0);
-        v = u32x4{e[0] | (uint32_t(e[1]) << 16), e[2] | (uint32_t(e[3]) << 16),
-                  e[4] | (uint32_t(e[5]) << 16), e[6] | (uint32_t(e[7]) << 16)};
-      }
-    }
-    *reinterpret_cast<u32x4 *>(lds + lds_piece_offset(row, piece)) = v;
-  }
+// Workgroup tile order.  Work-groups are handed to the 8 XCDs round-robin
+// (block b runs on XCD b % 8), and each XCD has its own L2.  Block b is
+// mapped to a logical tile index so that every XCD works through one
+// contiguous run of logical tiles, and logical tiles are ordered W-tile-major
+// (all X row blocks of one W tile are consecutive): the tiles an XCD runs at
+// the same time share W tiles, the large operand, in that XCD's L2.
+__device__ __forceinline__ void tile_of_block(int b, int tiles_n, int tiles_m, int &tn, int &tm) {
+  const int total = tiles_n * tiles_m;
+  const int xcd = b & 7, idx = b >> 3;
+  const int per = total >> 3, rem = total & 7;
+  const int t = (xcd < rem) ? xcd * (per + 1) + idx : rem * (per + 1) + (xcd - rem) * per + idx;
+  tn = t / tiles_m;
+  tm = t - tn * tiles_m;
 }
 
-// BN x BM tile of Z^T per workgroup; waves arranged WN x WM; each wave owns
-// (BN/WN) x (BM/WM) = FN x FM fragments of 16 x 16.
+// BN x BM tile of Z^T per workgroup (BN vocabulary rows of W, BM rows of X);
+// waves arranged WN x WM, each owning FN x FM fragments of 16 x 16.
+// K is walked in 64-wide steps through two LDS buffers: while the MFMAs of
+// step k read one buffer, the global loads of step k+1 are in flight into
+// registers, and are written to the other buffer afterwards (one barrier per
+// step).  In LDS, rows [0, BN) hold the W slice and rows [BN, BN+BM) the X
+// slice of the step.
 template <int BN, int BM, int WN, int WM, bool VEC>
 __global__ __launch_bounds__(kBlock) void lmhead_bf16_mfma(
     const uint16_t *__restrict__ X, int64_t M, int64_t K, const uint16_t *__restrict__ W,
-    int64_t N, uint16_t *__restrict__ out, int64_t ld, int64_t col_off) {
+    int64_t N, uint16_t *__restrict__ out, int64_t ld, int64_t col_off, int tiles_n,
+    int tiles_m) {
   static_assert(WN * WM == kBlock / 64, "4 waves per workgroup");
   constexpr int TN = BN / WN, TM = BM / WM;
   constexpr int FN = TN / 16, FM = TM / 16;
   static_assert(FN * 16 == TN && FM * 16 == TM, "wave tile must be a multiple of 16");
+  constexpr int kRows = BN + BM;
+  constexpr int kTilePieces = kRows * kPieces;
+  constexpr int kPiecesPerThread = (kTilePieces + kBlock - 1) / kBlock;
 
-  __shared__ __attribute__((aligned(16))) uint16_t sW[BN * BK];
-  __shared__ __attribute__((aligned(16))) uint16_t sX[BM * BK];
+  __shared__ __attribute__((aligned(16))) uint16_t lds[2][kRows * BK];
+
+  int tn, tm;
+  tile_of_block(blockIdx.x, tiles_n, tiles_m, tn, tm);
+  const int64_t n0 = static_cast<int64_t>(tn) * BN;
+  const int64_t m0 = static_cast<int64_t>(tm) * BM;
 
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int wn = wave % WN, wm = wave / WN;
-  const int64_t n0 = static_cast<int64_t>(blockIdx.x) * BN;
-  const int64_t m0 = static_cast<int64_t>(blockIdx.y) * BM;
+  const int frag_row = lane & 15;  // row of the fragment this lane feeds
+  const int frag_grp = lane >> 4;  // which 8-wide k group of a 32-wide step
+
+  // Staging: thread t copies piece t % 8 (8 k values) of tile rows
+  // t / 8 + 32 p, p = 0, 1, ...; tile rows [0, BN) are W rows n0 + r, rows
+  // [BN, BN + BM) are X rows m0 + r - BN.  BN is a multiple of 32, so each p
+  // falls wholly in the W part or the X part, and in LDS the pieces of one
+  // thread sit 32 rows (32 * BK elements) apart: the XOR swizzle depends on
+  // the row modulo 8 only.
+  static_assert(BN % 32 == 0, "W part of the tile must be a multiple of 32 rows");
+  constexpr int kRowsPerPass = kBlock / kPieces;  // 32
+  const int srow = threadIdx.x / kPieces;
+  const int spiece = threadIdx.x % kPieces;
+  const int64_t w_left = N - n0 - srow;        // W rows this thread may still stage
+  const int64_t x_left = M - m0 - srow;
+  const uint16_t *w_src = W + (w_left > 0 ? n0 + srow : 0) * K + spiece * 8;
+  const uint16_t *x_src = X + (x_left > 0 ? m0 + srow : 0) * K + spiece * 8;
+  const int lds_off0 = lds_piece_offset(srow, spiece);
+
+  // piece p of this thread is in range (row exists, k slice inside K)
+  auto piece_ok = [&](int p, int64_t k0) {
+    const int row = srow + p * kRowsPerPass;
+    const bool in_w = p * kRowsPerPass < BN;
+    const int64_t r = in_w ? p * kRowsPerPass : p * kRowsPerPass - BN;
+    return row < kRows && (in_w ? r < w_left : r < x_left) && k0 + spiece * 8 < K;
+  };
+  auto piece_src = [&](int p, int64_t k0) {
+    const bool in_w = p * kRowsPerPass < BN;
+    const int64_t r = in_w ? p * kRowsPerPass : p * kRowsPerPass - BN;
+    return (in_w ? w_src : x_src) + r * K + k0;
+  };
+
+  u32x4 pre[kPiecesPerThread];
+  // Loads only: out-of-range pieces are loaded from the operand's first row
+  // (always valid) and replaced by zeros when stored, so nothing waits on a
+  // load before the LDS store that needs it.
+  auto load_step = [&](int64_t k0) {
+#pragma unroll
+    for (int p = 0; p < kPiecesPerThread; ++p) {
+      if (VEC) {
+        const bool ok = piece_ok(p, k0);
+        const uint16_t *q = ok ? piece_src(p, k0) : ((p * kRowsPerPass < BN) ? W : X);
+        pre[p] = *reinterpret_cast<const u32x4 *>(q);
+      } else {
+        const int64_t gk = k0 + spiece * 8;
+        u32x4 v = u32x4(0);
+        if (piece_ok(p, k0)) {
+          const uint16_t *q = piece_src(p, k0);
+          uint16_t e[8];
+#pragma unroll
+          for (int i = 0; i < 8; ++i) e[i] = (gk + i < K) ? q[i] : uint16_t(0);
+          v = u32x4{e[0] | (uint32_t(e[1]) << 16), e[2] | (uint32_t(e[3]) << 16),
+                    e[4] | (uint32_t(e[5]) << 16), e[6] | (uint32_t(e[7]) << 16)};
+        }
+        pre[p] = v;
+      }
+    }
+  };
+  auto store_step = [&](uint16_t *buf, int64_t k0) {
+#pragma unroll
+    for (int p = 0; p < kPiecesPerThread; ++p)
+      if (srow + p * kRowsPerPass < kRows)
+        *reinterpret_cast<u32x4 *>(buf + lds_off0 + p * kRowsPerPass * BK) =
+            (!VEC || piece_ok(p, k0)) ? pre[p] : u32x4(0);
+  };
 
   f32x4 acc[FN][FM];
 #pragma unroll
@@ -108,53 +168,78 @@ __global__ __launch_bounds__(kBlock) void lmhead_bf16_mfma(
 #pragma unroll
     for (int j = 0; j < FM; ++j) acc[i][j] = f32x4(0.f);
 
-  const int frag_row = lane & 15;   // row of the fragment this lane feeds
-  const int frag_grp = lane >> 4;   // which 8-wide k group of a 32-wide step
-
-  for (int64_t k0 = 0; k0 < K; k0 += BK) {
-    __syncthreads();
-    stage_tile<BN, VEC>(sW, W, n0, N, K, k0);
-    stage_tile<BM, VEC>(sX, X, m0, M, K, k0);
-    __syncthreads();
+  const int64_t nk = (K + BK - 1) / BK;
+  load_step(0);
+  store_step(lds[0], 0);
+  __syncthreads();
+  for (int64_t kt = 0; kt < nk; ++kt) {
+    const uint16_t *cur = lds[kt & 1];
+    if (kt + 1 < nk) load_step((kt + 1) * BK);
+    // every fragment of the step is requested before the first MFMA: LDS
+    // returns in order, so MFMAs on the first 32-wide half start while the
+    // second half is still arriving
+    constexpr int KS = BK / 32;
+    bf16x8 a[KS][FN], b[KS][FM];
 #pragma unroll
-    for (int ks = 0; ks < BK / 32; ++ks) {
+    for (int ks = 0; ks < KS; ++ks) {
       const int piece = ks * 4 + frag_grp;
-      bf16x8 a[FN], b[FM];
 #pragma unroll
       for (int i = 0; i < FN; ++i)
-        a[i] = *reinterpret_cast<const bf16x8 *>(
-            sW + lds_piece_offset(wn * TN + i * 16 + frag_row, piece));
+        a[ks][i] = *reinterpret_cast<const bf16x8 *>(
+            cur + lds_piece_offset(wn * TN + i * 16 + frag_row, piece));
 #pragma unroll
       for (int j = 0; j < FM; ++j)
-        b[j] = *reinterpret_cast<const bf16x8 *>(
-            sX + lds_piece_offset(wm * TM + j * 16 + frag_row, piece));
-#pragma unroll
-      for (int i = 0; i < FN; ++i)
-#pragma unroll
-        for (int j = 0; j < FM; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+        b[ks][j] = *reinterpret_cast<const bf16x8 *>(
+            cur + lds_piece_offset(BN + wm * TM + j * 16 + frag_row, piece));
     }
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+      for (int j = 0; j < FM; ++j)
+#pragma unroll
+        for (int i = 0; i < FN; ++i)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[ks][i], b[ks][j], acc[i][j], 0, 0, 0);
+    // keep that order through scheduling: all LDS reads, then the MFMAs
+    __builtin_amdgcn_sched_group_barrier(0x100, KS * (FN + FM), 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, KS * FN * FM, 0);
+    if (kt + 1 < nk) store_step(lds[(kt + 1) & 1], (kt + 1) * BK);
+    __syncthreads();
   }
 
-  // acc[i][j][r] = Z^T[n = 4*(lane/16) + r][m = lane%16] of fragment (i, j)
+  // acc[i][j][r] = Z^T[n = 4*(lane/16) + r][m = lane%16] of fragment (i, j).
   // 8-byte stores need every row start at a multiple of 4 elements from an
-  // 8-byte-aligned base (column offsets inside a tile are multiples of 4)
+  // 8-byte-aligned base (column offsets inside a tile are multiples of 4).
   const bool pack_ok =
       ((ld | col_off) & 3) == 0 && (reinterpret_cast<uintptr_t>(out) & 7) == 0;
-#pragma unroll
-  for (int i = 0; i < FN; ++i) {
-    const int64_t n = n0 + wn * TN + i * 16 + 4 * frag_grp;
+  const int64_t nb = n0 + wn * TN + 4 * frag_grp;
+  const int64_t mb = m0 + wm * TM + frag_row;
+  if (pack_ok && n0 + BN <= N && m0 + BM <= M) {
+    // whole tile in range: no per-element checks
 #pragma unroll
     for (int j = 0; j < FM; ++j) {
-      const int64_t m = m0 + wm * TM + j * 16 + frag_row;
-      if (m >= M) continue;
+      uint16_t *row = out + (mb + j * 16) * ld + col_off + nb;
+#pragma unroll
+      for (int i = 0; i < FN; ++i) {
+        const u32x2 v{f32_to_bf16_bits(acc[i][j][0]) | (f32_to_bf16_bits(acc[i][j][1]) << 16),
+                      f32_to_bf16_bits(acc[i][j][2]) | (f32_to_bf16_bits(acc[i][j][3]) << 16)};
+        *reinterpret_cast<u32x2 *>(row + i * 16) = v;
+      }
+    }
+    return;
+  }
+#pragma unroll
+  for (int j = 0; j < FM; ++j) {
+    const int64_t m = mb + j * 16;
+    if (m >= M) continue;
+#pragma unroll
+    for (int i = 0; i < FN; ++i) {
+      const int64_t n = nb + i * 16;
       uint16_t *dst = out + m * ld + col_off + n;
       if (pack_ok && n + 3 < N) {
         const u32x2 v{f32_to_bf16_bits(acc[i][j][0]) | (f32_to_bf16_bits(acc[i][j][1]) << 16),
                       f32_to_bf16_bits(acc[i][j][2]) | (f32_to_bf16_bits(acc[i][j][3]) << 16)};
         *reinterpret_cast<u32x2 *>(dst) = v;
       } else {
-#pragma unroll
         for (int r = 0; r < 4; ++r)
           if (n + r < N) dst[r] = static_cast<uint16_t>(f32_to_bf16_bits(acc[i][j][r]));
       }
@@ -211,16 +296,21 @@ __global__ __launch_bounds__(kBlock) void lmhead_f32_tiled(const float *__restri
 }
 
 template <int BN, int BM, int WN, int WM>
-void launch_bf16_cfg(const uint16_t *x, int64_t m, int64_t k, const uint16_t *w, int64_t n,
-                     uint16_t *out, int64_t ld, int64_t col_off, hipStream_t st) {
-  const dim3 grid(static_cast<unsigned>((n + BN - 1) / BN), static_cast<unsigned>((m + BM - 1) / BM));
+int launch_bf16_cfg(const uint16_t *x, int64_t m, int64_t k, const uint16_t *w, int64_t n,
+                    uint16_t *out, int64_t ld, int64_t col_off, hipStream_t st) {
+  const int64_t tn64 = (n + BN - 1) / BN, tm64 = (m + BM - 1) / BM;
+  if (tn64 * tm64 > INT32_MAX) return static_cast<int>(hipErrorInvalidValue);
+  const int tiles_n = static_cast<int>(tn64);
+  const int tiles_m = static_cast<int>(tm64);
+  const dim3 grid(static_cast<unsigned>(tiles_n) * static_cast<unsigned>(tiles_m));
   const bool vec = (k % 8 == 0) && ((reinterpret_cast<uint64_t>(x) | reinterpret_cast<uint64_t>(w)) & 15) == 0;
   if (vec)
     hipLaunchKernelGGL((lmhead_bf16_mfma<BN, BM, WN, WM, true>), grid, dim3(kBlock), 0, st, x, m,
-                       k, w, n, out, ld, col_off);
+                       k, w, n, out, ld, col_off, tiles_n, tiles_m);
   else
     hipLaunchKernelGGL((lmhead_bf16_mfma<BN, BM, WN, WM, false>), grid, dim3(kBlock), 0, st, x,
-                       m, k, w, n, out, ld, col_off);
+                       m, k, w, n, out, ld, col_off, tiles_n, tiles_m);
+  return 0;
 }
 
 }  // namespace
@@ -239,14 +329,20 @@ int launch_lmhead(const void *x, int64_t m, int64_t k, const void *w, int64_t n,
   const uint16_t *xb = static_cast<const uint16_t *>(x);
   const uint16_t *wb = static_cast<const uint16_t *>(w);
   uint16_t *ob = static_cast<uint16_t *>(logits);
+  int rc;
   if (m <= 16)
-    launch_bf16_cfg<128, 16, 4, 1>(xb, m, k, wb, n, ob, ld, col_offset, st);
+    rc = launch_bf16_cfg<256, 16, 4, 1>(xb, m, k, wb, n, ob, ld, col_offset, st);
   else if (m <= 32)
-    launch_bf16_cfg<128, 32, 4, 1>(xb, m, k, wb, n, ob, ld, col_offset, st);
+    rc = launch_bf16_cfg<256, 32, 4, 1>(xb, m, k, wb, n, ob, ld, col_offset, st);
   else if (m <= 64)
-    launch_bf16_cfg<128, 64, 4, 1>(xb, m, k, wb, n, ob, ld, col_offset, st);
+    rc = launch_bf16_cfg<256, 64, 4, 1>(xb, m, k, wb, n, ob, ld, col_offset, st);
+  else if (m <= 128)
+    rc = launch_bf16_cfg<256, 128, 2, 2>(xb, m, k, wb, n, ob, ld, col_offset, st);
+  else if (m <= 256)
+    rc = launch_bf16_cfg<128, 256, 2, 2>(xb, m, k, wb, n, ob, ld, col_offset, st);
   else
-    launch_bf16_cfg<128, 128, 2, 2>(xb, m, k, wb, n, ob, ld, col_offset, st);
+    rc = launch_bf16_cfg<256, 256, 2, 2>(xb, m, k, wb, n, ob, ld, col_offset, st);
+  if (rc != 0) return rc;
   return static_cast<int>(hipGetLastError());
 }
 
