@@ -47,6 +47,9 @@ def parse_args():
                    help="input copies to rotate through (0 = enough for >= 1 GiB)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-threads", type=int, default=0, help="0 = min(16, cores available)")
+    p.add_argument("--copy-probe-mib", type=int, default=0,
+                   help="after timing, run one device-to-device copy of this many MiB "
+                        "(a reference kernel for hardware byte counters)")
     return p.parse_args()
 
 
@@ -192,6 +195,13 @@ def main():
             run_step(k, evs[k])
         torch.cuda.synchronize()
         t_total = time.perf_counter() - t_start
+
+    if args.copy_probe_mib:
+        src = torch.empty(args.copy_probe_mib << 20, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     kinds = [c[0] for c in calls[0]]
     per_kind_ms = {}

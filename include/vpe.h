@@ -166,7 +166,7 @@ vpe_status vpe_last_token_select(const void *hidden, int64_t n_tokens, int64_t d
  * `dt` (round to nearest, ties to even).
  * m == 0 is a no-op.
  * Errors: VPE_ERR_NULL, VPE_ERR_SHAPE (m < 0, m > 2^21, dim < 1,
- * shard_rows < 1), VPE_ERR_RANGE (col_offset < 0 or col_offset + shard_rows > ld_out),
+ * dim > 2^20, shard_rows < 1), VPE_ERR_RANGE (col_offset < 0 or col_offset + shard_rows > ld_out),
  * VPE_ERR_DTYPE, VPE_ERR_ALIGN.
  */
 vpe_status vpe_lmhead(const void *x, int64_t m, int64_t dim, const void *weight,

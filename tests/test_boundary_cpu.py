@@ -124,6 +124,7 @@ def test_lmhead_validation():
     assert call(dim=0) == vpe.VPE_ERR_SHAPE
     assert call(rows=0) == vpe.VPE_ERR_SHAPE
     assert call(m=2 ** 21 + 1) == vpe.VPE_ERR_SHAPE
+    assert call(dim=2 ** 20 + 8) == vpe.VPE_ERR_SHAPE
     assert call(ld=99) == vpe.VPE_ERR_RANGE
     assert call(ld=150, col=51) == vpe.VPE_ERR_RANGE
     assert call(col=-1, ld=200) == vpe.VPE_ERR_RANGE

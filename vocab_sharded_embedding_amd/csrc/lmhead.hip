@@ -31,6 +31,8 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kBlock = 256;
+// dword 3 of a gfx9 buffer descriptor: 32-bit data format, raw (unswizzled) access
+constexpr int kBufferFlags = 0x00020000;
 
 // binary32 -> bf16 bits, round to nearest, ties to even; NaN becomes a quiet NaN
 __device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
@@ -40,56 +42,101 @@ __device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
 }
 
 // ---------------------------------------------------------------------------
-// LDS tile layout: rows of BK = 64 bf16 (128 bytes = 8 pieces of 16 bytes).
-// Piece p of row r is stored at piece slot p ^ (r & 7), so the 16 rows one
-// MFMA fragment reads at the same k land in 8 different bank groups.
+// LDS tile layout: a row holds BK bf16 = BK/8 pieces of 16 bytes.  Piece p of
+// row r is stored at slot p ^ f(r), f(r) = r mod P (SWZ 0) or (r/2) mod P
+// (SWZ 1), P = BK/8: the 16 rows one MFMA fragment reads at the same k then
+// fall in different LDS banks.
 // ---------------------------------------------------------------------------
-constexpr int BK = 64;
-constexpr int kPieces = BK / 8;
-
+template <int BK, int SWZ>
 __device__ __forceinline__ int lds_piece_offset(int row, int piece) {
-  return row * BK + ((piece ^ (row & 7)) << 3);  // in bf16 elements
+  constexpr int P = BK / 8;
+  const int f = (SWZ == 0) ? (row & (P - 1)) : ((row >> 1) & (P - 1));
+  return row * BK + ((piece ^ f) << 3);  // in bf16 elements
 }
 
 // Workgroup tile order.  Work-groups are handed to the 8 XCDs round-robin
 // (block b runs on XCD b % 8), and each XCD has its own L2.  Block b is
 // mapped to a logical tile index so that every XCD works through one
-// contiguous run of logical tiles, and logical tiles are ordered W-tile-major
-// (all X row blocks of one W tile are consecutive): the tiles an XCD runs at
-// the same time share W tiles, the large operand, in that XCD's L2.
-__device__ __forceinline__ void tile_of_block(int b, int tiles_n, int tiles_m, int &tn, int &tm) {
+// contiguous run of logical tiles.  Logical tiles are ordered in groups of
+// GN W tiles: inside a group, X row blocks are the outer index and the GN W
+// tiles the inner one.  The ~32 tiles an XCD runs at once then cover GN W
+// tiles times 32/GN X tiles, so both operands are shared in that XCD's L2
+// (GN = 1: all X blocks of one W tile, the order for few X blocks).
+__device__ __forceinline__ void tile_of_block(int b, int tiles_n, int tiles_m, int group_n,
+                                              int &tn, int &tm) {
   const int total = tiles_n * tiles_m;
   const int xcd = b & 7, idx = b >> 3;
   const int per = total >> 3, rem = total & 7;
   const int t = (xcd < rem) ? xcd * (per + 1) + idx : rem * (per + 1) + (xcd - rem) * per + idx;
-  tn = t / tiles_m;
-  tm = t - tn * tiles_m;
+  const int per_group = group_n * tiles_m;
+  const int g = t / per_group;
+  const int in_g = t - g * per_group;
+  const int gn = min(group_n, tiles_n - g * group_n);  // the last group may be narrower
+  tm = in_g / gn;
+  tn = g * group_n + (in_g - tm * gn);
 }
 
-// BN x BM tile of Z^T per workgroup (BN vocabulary rows of W, BM rows of X);
-// waves arranged WN x WM, each owning FN x FM fragments of 16 x 16.
-// K is walked in 64-wide steps through two LDS buffers: while the MFMAs of
-// step k read one buffer, the global loads of step k+1 are in flight into
-// registers, and are written to the other buffer afterwards (one barrier per
-// step).  In LDS, rows [0, BN) hold the W slice and rows [BN, BN+BM) the X
-// slice of the step.
-template <int BN, int BM, int WN, int WM, bool VEC>
-__global__ __launch_bounds__(kBlock) void lmhead_bf16_mfma(
+// Tile configuration of the bf16 kernel.
+//   BN x BM   tile of Z^T per workgroup (BN vocabulary rows of W, BM rows of X)
+//   WN x WM   arrangement of the 4 waves; a wave owns (BN/WN) x (BM/WM)
+//   BK        K slice per pipeline step (64 or 128)
+//   PF        register sets for staged global data (loads run ahead by
+//             max(PF, 2) steps: 1 set = the next step's loads are issued
+//             halfway through the current step's MFMAs)
+//   SWZ       LDS swizzle variant (see lds_piece_offset)
+//   RS        fragment read schedule: 0 = every fragment of a step read
+//             before its first MFMA; 1 = the second 32-wide half's fragments
+//             are read while the first half's MFMAs run (fewer live registers)
+//   PIPE      0: two LDS buffers, a step's fragments are read after the
+//             barrier that opens it; 1: three LDS buffers and two fragment
+//             register sets, so a step's MFMAs use fragments read during the
+//             previous step and never wait on LDS after a barrier;
+//             2: NS LDS stages filled by buffer loads that write LDS directly
+//             (no staging registers), NS-1 steps in flight
+//   NS        LDS stages of PIPE 2
+// The workgroup has WN * WM waves of 64 lanes.
+template <int BN_, int BM_, int WN_, int WM_, int BK_, int PF_, int SWZ_ = 0, int RS_ = 0,
+          int PIPE_ = 0, int NS_ = 3>
+struct Cfg {
+  static constexpr int BN = BN_, BM = BM_, WN = WN_, WM = WM_, BK = BK_, PF = PF_, SWZ = SWZ_;
+  static constexpr int RS = RS_, PIPE = PIPE_, NS = NS_;
+  static constexpr int NT = WN_ * WM_ * 64;
+};
+
+// s_waitcnt immediate that waits until at most n vector-memory operations of
+// this wave are outstanding (LDS and export counters left alone).
+constexpr int vmcnt_imm(int n) { return (n & 0xF) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8); }
+
+// Z^T tile = W_tile . X_tile^T over K, staged through two LDS buffers.
+// Each step: barrier; read every MFMA fragment of step k from one buffer;
+// write step k+1 (already in registers) to the other buffer; issue the
+// global loads of a later step; run the MFMAs.  One barrier per step, and
+// the LDS writes and global loads overlap the MFMAs.  In LDS, rows [0, BN)
+// hold the W slice and rows [BN, BN+BM) the X slice of a step.
+template <class C, bool VEC>
+__global__ __launch_bounds__(C::NT) void lmhead_bf16_mfma(
     const uint16_t *__restrict__ X, int64_t M, int64_t K, const uint16_t *__restrict__ W,
     int64_t N, uint16_t *__restrict__ out, int64_t ld, int64_t col_off, int tiles_n,
-    int tiles_m) {
-  static_assert(WN * WM == kBlock / 64, "4 waves per workgroup");
+    int tiles_m, int group_n) {
+  constexpr int BN = C::BN, BM = C::BM, WN = C::WN, WM = C::WM, BK = C::BK, PF = C::PF;
+  constexpr int SWZ = C::SWZ, RS = C::RS, NT = C::NT, PIPE = C::PIPE;
   constexpr int TN = BN / WN, TM = BM / WM;
   constexpr int FN = TN / 16, FM = TM / 16;
   static_assert(FN * 16 == TN && FM * 16 == TM, "wave tile must be a multiple of 16");
+  constexpr int kPieces = BK / 8;                  // 16-byte pieces per row
+  constexpr int kRowsPerPass = NT / kPieces;       // rows staged per pass of the block
   constexpr int kRows = BN + BM;
-  constexpr int kTilePieces = kRows * kPieces;
-  constexpr int kPiecesPerThread = (kTilePieces + kBlock - 1) / kBlock;
+  constexpr int kPPT = (kRows + kRowsPerPass - 1) / kRowsPerPass;  // pieces per thread
+  constexpr int KS = BK / 32;                      // MFMA k-steps per pipeline step
 
-  __shared__ __attribute__((aligned(16))) uint16_t lds[2][kRows * BK];
+  // PIPE 2 pads a stage to whole passes: every lane of a load writes inside it
+  constexpr int kNumBuf = PIPE == 2 ? C::NS : (PIPE ? 3 : 2);
+  constexpr int kBufElems = (PIPE == 2 ? kPPT * kRowsPerPass : kRows) * BK;
+  __shared__ __attribute__((aligned(16))) uint16_t lds_all[kNumBuf * kBufElems];
+  uint16_t(*lds)[kBufElems] = reinterpret_cast<uint16_t(*)[kBufElems]>(lds_all);
 
   int tn, tm;
-  tile_of_block(blockIdx.x, tiles_n, tiles_m, tn, tm);
+  tile_of_block(blockIdx.x, tiles_n, tiles_m, group_n, tn, tm);
   const int64_t n0 = static_cast<int64_t>(tn) * BN;
   const int64_t m0 = static_cast<int64_t>(tm) * BM;
 
@@ -99,67 +146,69 @@ __global__ __launch_bounds__(kBlock) void lmhead_bf16_mfma(
   const int frag_row = lane & 15;  // row of the fragment this lane feeds
   const int frag_grp = lane >> 4;  // which 8-wide k group of a 32-wide step
 
-  // Staging: thread t copies piece t % 8 (8 k values) of tile rows
-  // t / 8 + 32 p, p = 0, 1, ...; tile rows [0, BN) are W rows n0 + r, rows
-  // [BN, BN + BM) are X rows m0 + r - BN.  BN is a multiple of 32, so each p
-  // falls wholly in the W part or the X part, and in LDS the pieces of one
-  // thread sit 32 rows (32 * BK elements) apart: the XOR swizzle depends on
-  // the row modulo 8 only.
-  static_assert(BN % 32 == 0, "W part of the tile must be a multiple of 32 rows");
-  constexpr int kRowsPerPass = kBlock / kPieces;  // 32
+  // Staging: thread t copies piece t % P of tile rows t / P + kRowsPerPass*p.
   const int srow = threadIdx.x / kPieces;
   const int spiece = threadIdx.x % kPieces;
-  const int64_t w_left = N - n0 - srow;        // W rows this thread may still stage
-  const int64_t x_left = M - m0 - srow;
-  const uint16_t *w_src = W + (w_left > 0 ? n0 + srow : 0) * K + spiece * 8;
-  const uint16_t *x_src = X + (x_left > 0 ? m0 + srow : 0) * K + spiece * 8;
-  const int lds_off0 = lds_piece_offset(srow, spiece);
+  const int64_t nk = (K + BK - 1) / BK;
+  const int64_t w_rows = (N - n0 < BN) ? N - n0 : BN;  // rows of this tile inside W / X
+  const int64_t x_rows = (M - m0 < BM) ? M - m0 : BM;
 
-  // piece p of this thread is in range (row exists, k slice inside K)
-  auto piece_ok = [&](int p, int64_t k0) {
-    const int row = srow + p * kRowsPerPass;
-    const bool in_w = p * kRowsPerPass < BN;
-    const int64_t r = in_w ? p * kRowsPerPass : p * kRowsPerPass - BN;
-    return row < kRows && (in_w ? r < w_left : r < x_left) && k0 + spiece * 8 < K;
-  };
-  auto piece_src = [&](int p, int64_t k0) {
-    const bool in_w = p * kRowsPerPass < BN;
-    const int64_t r = in_w ? p * kRowsPerPass : p * kRowsPerPass - BN;
-    return (in_w ? w_src : x_src) + r * K + k0;
-  };
+  // VEC staging reads through buffer descriptors over this tile's rows: the
+  // hardware range check returns zeros for rows past the end of W or X, the
+  // row offset is one 32-bit register, and the K offset of a step is scalar.
+  const __amdgpu_buffer_rsrc_t w_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t *>(W + n0 * K), 0, static_cast<int>(w_rows * K * 2), kBufferFlags);
+  const __amdgpu_buffer_rsrc_t x_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t *>(X + m0 * K), 0, static_cast<int>(x_rows * K * 2), kBufferFlags);
+  const int row_bytes = static_cast<int>(K * 2);
+  const int voff0 = srow * row_bytes + spiece * 16;
+  const int row_stride_bytes = kRowsPerPass * row_bytes;
 
-  u32x4 pre[kPiecesPerThread];
-  // Loads only: out-of-range pieces are loaded from the operand's first row
-  // (always valid) and replaced by zeros when stored, so nothing waits on a
-  // load before the LDS store that needs it.
-  auto load_step = [&](int64_t k0) {
+  u32x4 pre[PF][kPPT];
+  // Loads only; nothing waits on them before the LDS write that needs them.
+  // Steps past the end are clamped to the last step (their data is unused).
+  auto load_step = [&](u32x4 (&dst)[kPPT], int64_t step) {
+    const int64_t k0 = (step < nk ? step : nk - 1) * BK;
 #pragma unroll
-    for (int p = 0; p < kPiecesPerThread; ++p) {
+    for (int p = 0; p < kPPT; ++p) {
+      // tile row of this piece; passes that straddle the W/X boundary decide per lane
+      const int row = srow + p * kRowsPerPass;
+      const bool in_w = (BN % kRowsPerPass == 0) ? (p * kRowsPerPass < BN) : (row < BN);
+      const int r = in_w ? row : row - BN;  // row inside W's or X's part of the tile
       if (VEC) {
-        const bool ok = piece_ok(p, k0);
-        const uint16_t *q = ok ? piece_src(p, k0) : ((p * kRowsPerPass < BN) ? W : X);
-        pre[p] = *reinterpret_cast<const u32x4 *>(q);
+        const int voff = (BN % kRowsPerPass == 0)
+                             ? voff0 + (in_w ? p : p - BN / kRowsPerPass) * row_stride_bytes
+                             : r * row_bytes + spiece * 16;
+        dst[p] = __builtin_amdgcn_raw_buffer_load_b128(in_w ? w_rsrc : x_rsrc, voff,
+                                                       static_cast<int>(k0 * 2), 0);
       } else {
         const int64_t gk = k0 + spiece * 8;
         u32x4 v = u32x4(0);
-        if (piece_ok(p, k0)) {
-          const uint16_t *q = piece_src(p, k0);
+        if (row < kRows && r < (in_w ? w_rows : x_rows)) {
+          const uint16_t *q = (in_w ? W + (n0 + r) * K : X + (m0 + r) * K) + gk;
           uint16_t e[8];
 #pragma unroll
           for (int i = 0; i < 8; ++i) e[i] = (gk + i < K) ? q[i] : uint16_t(0);
           v = u32x4{e[0] | (uint32_t(e[1]) << 16), e[2] | (uint32_t(e[3]) << 16),
                     e[4] | (uint32_t(e[5]) << 16), e[6] | (uint32_t(e[7]) << 16)};
         }
-        pre[p] = v;
+        dst[p] = v;
       }
     }
   };
-  auto store_step = [&](uint16_t *buf, int64_t k0) {
+  // A step's last K slice may run past K (K is a multiple of 8 on the VEC
+  // path, so a piece is either inside K or wholly past it): those pieces read
+  // the next row's data through the buffer and are zeroed here.
+  auto store_step = [&](const u32x4 (&src)[kPPT], uint16_t *buf, int64_t step) {
+    const int64_t k0 = (step < nk ? step : nk - 1) * BK;
+    const bool k_in = k0 + spiece * 8 < K;
 #pragma unroll
-    for (int p = 0; p < kPiecesPerThread; ++p)
-      if (srow + p * kRowsPerPass < kRows)
-        *reinterpret_cast<u32x4 *>(buf + lds_off0 + p * kRowsPerPass * BK) =
-            (!VEC || piece_ok(p, k0)) ? pre[p] : u32x4(0);
+    for (int p = 0; p < kPPT; ++p) {
+      const int row = srow + p * kRowsPerPass;
+      if (kRows % kRowsPerPass == 0 || row < kRows)
+        *reinterpret_cast<u32x4 *>(buf + lds_piece_offset<BK, SWZ>(row, spiece)) =
+            (!VEC || k_in) ? src[p] : u32x4(0);
+    }
   };
 
   f32x4 acc[FN][FM];
@@ -168,43 +217,176 @@ __global__ __launch_bounds__(kBlock) void lmhead_bf16_mfma(
 #pragma unroll
     for (int j = 0; j < FM; ++j) acc[i][j] = f32x4(0.f);
 
-  const int64_t nk = (K + BK - 1) / BK;
-  load_step(0);
-  store_step(lds[0], 0);
-  __syncthreads();
-  for (int64_t kt = 0; kt < nk; ++kt) {
-    const uint16_t *cur = lds[kt & 1];
-    if (kt + 1 < nk) load_step((kt + 1) * BK);
-    // every fragment of the step is requested before the first MFMA: LDS
-    // returns in order, so MFMAs on the first 32-wide half start while the
-    // second half is still arriving
-    constexpr int KS = BK / 32;
-    bf16x8 a[KS][FN], b[KS][FM];
+  bf16x8 fa[PIPE ? 2 : 1][KS][FN], fb[PIPE ? 2 : 1][KS][FM];
+  auto read_frags_set = [&](int set, const uint16_t *cur, int ks0, int ks1) {
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
+    for (int ks = ks0; ks < ks1; ++ks) {
       const int piece = ks * 4 + frag_grp;
 #pragma unroll
       for (int i = 0; i < FN; ++i)
-        a[ks][i] = *reinterpret_cast<const bf16x8 *>(
-            cur + lds_piece_offset(wn * TN + i * 16 + frag_row, piece));
+        fa[set][ks][i] = *reinterpret_cast<const bf16x8 *>(
+            cur + lds_piece_offset<BK, SWZ>(wn * TN + i * 16 + frag_row, piece));
 #pragma unroll
       for (int j = 0; j < FM; ++j)
-        b[ks][j] = *reinterpret_cast<const bf16x8 *>(
-            cur + lds_piece_offset(BN + wm * TM + j * 16 + frag_row, piece));
+        fb[set][ks][j] = *reinterpret_cast<const bf16x8 *>(
+            cur + lds_piece_offset<BK, SWZ>(BN + wm * TM + j * 16 + frag_row, piece));
     }
+  };
+  auto mfma_set = [&](int set, int ks0, int ks1) {
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
+    for (int ks = ks0; ks < ks1; ++ks)
 #pragma unroll
       for (int j = 0; j < FM; ++j)
 #pragma unroll
         for (int i = 0; i < FN; ++i)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[ks][i], b[ks][j], acc[i][j], 0, 0, 0);
-    // keep that order through scheduling: all LDS reads, then the MFMAs
-    __builtin_amdgcn_sched_group_barrier(0x100, KS * (FN + FM), 0);
-    __builtin_amdgcn_sched_group_barrier(0x008, KS * FN * FM, 0);
-    if (kt + 1 < nk) store_step(lds[(kt + 1) & 1], (kt + 1) * BK);
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[set][ks][i], fb[set][ks][j],
+                                                              acc[i][j], 0, 0, 0);
+  };
+  auto read_frags = [&](const uint16_t *cur, int ks0, int ks1) { read_frags_set(0, cur, ks0, ks1); };
+  auto mfma_range = [&](int ks0, int ks1) { mfma_set(0, ks0, ks1); };
+
+  if constexpr (PIPE == 2 && VEC) {
+    constexpr int NS = C::NS;
+    constexpr int kRowsPerWaveLoad = 64 / kPieces;  // rows one wave load instruction fills
+    static_assert(BN % kRowsPerWaveLoad == 0, "a load instruction must stay inside W or X");
+    static_assert((NS - 2) * kPPT <= 63, "outstanding loads must fit the vmcnt counter");
+    const int wave_u = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6);
+    const int lrow = lane / kPieces, lslot = lane % kPieces;
+    constexpr int kBig = 0x7FFF0000;  // offset past any descriptor's range: loads return 0
+    const int nk_i = static_cast<int>(nk);
+    const int k_i = static_cast<int>(K);
+    const int w_rows_i = static_cast<int>(w_rows), x_rows_i = static_cast<int>(x_rows);
+    // One step into stage buffer `buf`: lane l of wave w fills LDS slot l % P
+    // of tile row p * kRowsPerPass + w * (64 / P) + l / P, which holds piece
+    // slot ^ f(row) of that row (the swizzle is applied on the global side).
+    auto dma_step = [&](int step, int buf) {
+      const int k0 = (step < nk_i ? step : nk_i - 1) * BK;
+      uint16_t *base = lds[buf];
+#pragma unroll
+      for (int p = 0; p < kPPT; ++p) {
+        const int row0 = p * kRowsPerPass + wave_u * kRowsPerWaveLoad;  // wave-uniform
+        const int row = row0 + lrow;
+        const int piece = lslot ^ ((SWZ == 0) ? (row & (kPieces - 1)) : ((row >> 1) & (kPieces - 1)));
+        bool in_w;
+        if constexpr (BN % kRowsPerPass == 0) in_w = p * kRowsPerPass < BN;
+        else in_w = row0 < BN;
+        const int r = in_w ? row : row - BN;
+        const bool ok = r < (in_w ? w_rows_i : x_rows_i) && k0 + piece * 8 < k_i;
+        const int voff = ok ? r * row_bytes + piece * 16 : kBig;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            in_w ? w_rsrc : x_rsrc, (__attribute__((address_space(3))) void *)(base + row0 * BK),
+            16, voff, k0 * 2, 0, 0);
+      }
+    };
+#pragma unroll
+    for (int st = 0; st < NS - 1; ++st) dma_step(st, st);
+    int rd = 0, wr = NS - 1;  // stage buffers read and refilled by the current step
+    for (int kt = 0; kt < nk_i; ++kt) {
+      // this wave's loads of step kt have landed once at most the later
+      // NS-2 steps' loads are outstanding; the barrier extends that to all
+      // waves and also closes every wave's reads of step kt-1's buffer
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm((NS - 2) * kPPT));
+      asm volatile("s_barrier" ::: "memory");
+      dma_step(kt + NS - 1, wr);
+      read_frags(lds[rd], 0, KS);
+      mfma_range(0, KS);
+      rd = (rd + 1 == NS) ? 0 : rd + 1;
+      wr = (wr + 1 == NS) ? 0 : wr + 1;
+    }
+  } else if constexpr (PIPE == 1) {
+    // (PIPE 2 without 16-byte-aligned rows takes the PIPE 0 path below)
+    static_assert(PF <= 2, "the three-buffer pipeline keeps at most two register sets");
+    // prologue: steps 0 and 1 in LDS buffers 0 and 1, step 2 in registers,
+    // step 0's fragments in register set 0
+    load_step(pre[0], 0);
+    store_step(pre[0], lds[0], 0);
+    load_step(pre[PF - 1], 1);
+    store_step(pre[PF - 1], lds[1], 1);
+    load_step(pre[0], 2);
     __syncthreads();
+    read_frags_set(0, lds[0], 0, KS);
+    for (int64_t kb = 0; kb < nk; kb += 2) {
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int64_t kt = kb + u;
+        if (kt >= nk) break;
+        __syncthreads();
+        // buffer (kt+1)%3 holds step kt+1 (written one step ago); buffer
+        // (kt+2)%3 held step kt-1, whose fragments were read two steps ago
+        read_frags_set(1 - u, lds[(kt + 1) % 3], 0, KS);
+        store_step(pre[PF == 1 ? 0 : u], lds[(kt + 2) % 3], kt + 2);
+        load_step(pre[PF == 1 ? 0 : 1 - u], kt + 3);
+        mfma_set(u, 0, KS);
+        __builtin_amdgcn_sched_group_barrier(0x100, KS * (FN + FM), 0);  // LDS reads
+        __builtin_amdgcn_sched_group_barrier(0x200, kPPT, 0);            // LDS writes
+        __builtin_amdgcn_sched_group_barrier(0x020, kPPT, 0);            // global loads
+        __builtin_amdgcn_sched_group_barrier(0x008, KS * FN * FM, 0);    // MFMAs
+      }
+    }
+  } else {
+  // prologue: step 0 in LDS buffer 0, steps 1 .. max(PF,2)-1 in registers
+  load_step(pre[0], 0);
+  store_step(pre[0], lds[0], 0);
+  if constexpr (PF == 1) {
+    load_step(pre[0], 1);
+  } else {
+#pragma unroll
+    for (int j = 1; j < PF; ++j) load_step(pre[j], j);
   }
+
+  for (int64_t kb = 0; kb < nk; kb += PF) {
+#pragma unroll
+    for (int u = 0; u < PF; ++u) {
+      const int64_t kt = kb + u;
+      if (kt >= nk) break;
+      __syncthreads();
+      const uint16_t *cur = lds[kt & 1];
+      if constexpr (RS == 0) {
+        read_frags(cur, 0, KS);
+        // step kt+1 sits in register set (kt+1) % PF
+        store_step(pre[(u + 1) % PF], lds[(kt + 1) & 1], kt + 1);
+        if constexpr (PF == 1) {
+          mfma_range(0, KS / 2);
+          load_step(pre[0], kt + 2);
+          mfma_range(KS / 2, KS);
+          __builtin_amdgcn_sched_group_barrier(0x100, KS * (FN + FM), 0);  // LDS reads
+          __builtin_amdgcn_sched_group_barrier(0x200, kPPT, 0);            // LDS writes
+          __builtin_amdgcn_sched_group_barrier(0x008, (KS / 2) * FN * FM, 0);
+          __builtin_amdgcn_sched_group_barrier(0x020, kPPT, 0);            // global loads
+          __builtin_amdgcn_sched_group_barrier(0x008, (KS - KS / 2) * FN * FM, 0);
+        } else {
+          // set kt % PF held step kt, written to LDS one step ago: refill it
+          load_step(pre[u], kt + PF);
+          mfma_range(0, KS);
+          __builtin_amdgcn_sched_group_barrier(0x100, KS * (FN + FM), 0);
+          __builtin_amdgcn_sched_group_barrier(0x200, kPPT, 0);
+          __builtin_amdgcn_sched_group_barrier(0x020, kPPT, 0);
+          __builtin_amdgcn_sched_group_barrier(0x008, KS * FN * FM, 0);
+        }
+      } else {
+        // first half's fragments, LDS writes, first half's MFMAs with the
+        // second half's fragment reads slotted in before their end
+        constexpr int H = KS / 2;
+        constexpr int kMf0 = H * FN * FM;
+        constexpr int kLate = (kMf0 / 4 > 0) ? kMf0 / 4 : 1;  // MFMAs after the late reads
+        read_frags(cur, 0, H);
+        store_step(pre[(u + 1) % PF], lds[(kt + 1) & 1], kt + 1);
+        mfma_range(0, H);
+        read_frags(cur, H, KS);
+        if constexpr (PF == 1) load_step(pre[0], kt + 2);
+        else load_step(pre[u], kt + PF);
+        mfma_range(H, KS);
+        __builtin_amdgcn_sched_group_barrier(0x100, H * (FN + FM), 0);
+        __builtin_amdgcn_sched_group_barrier(0x200, kPPT, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, kMf0 - kLate, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, (KS - H) * (FN + FM), 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, kLate, 0);
+        __builtin_amdgcn_sched_group_barrier(0x020, kPPT, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, (KS - H) * FN * FM, 0);
+      }
+    }
+  }
+  }  // PIPE == 0
 
   // acc[i][j][r] = Z^T[n = 4*(lane/16) + r][m = lane%16] of fragment (i, j).
   // 8-byte stores need every row start at a multiple of 4 elements from an
@@ -295,21 +477,21 @@ __global__ __launch_bounds__(kBlock) void lmhead_f32_tiled(const float *__restri
   }
 }
 
-template <int BN, int BM, int WN, int WM>
+template <class C>
 int launch_bf16_cfg(const uint16_t *x, int64_t m, int64_t k, const uint16_t *w, int64_t n,
-                    uint16_t *out, int64_t ld, int64_t col_off, hipStream_t st) {
-  const int64_t tn64 = (n + BN - 1) / BN, tm64 = (m + BM - 1) / BM;
+                    uint16_t *out, int64_t ld, int64_t col_off, hipStream_t st, int group_n = 1) {
+  const int64_t tn64 = (n + C::BN - 1) / C::BN, tm64 = (m + C::BM - 1) / C::BM;
   if (tn64 * tm64 > INT32_MAX) return static_cast<int>(hipErrorInvalidValue);
   const int tiles_n = static_cast<int>(tn64);
   const int tiles_m = static_cast<int>(tm64);
   const dim3 grid(static_cast<unsigned>(tiles_n) * static_cast<unsigned>(tiles_m));
   const bool vec = (k % 8 == 0) && ((reinterpret_cast<uint64_t>(x) | reinterpret_cast<uint64_t>(w)) & 15) == 0;
   if (vec)
-    hipLaunchKernelGGL((lmhead_bf16_mfma<BN, BM, WN, WM, true>), grid, dim3(kBlock), 0, st, x, m,
-                       k, w, n, out, ld, col_off, tiles_n, tiles_m);
+    hipLaunchKernelGGL((lmhead_bf16_mfma<C, true>), grid, dim3(C::NT), 0, st, x, m, k, w, n, out,
+                       ld, col_off, tiles_n, tiles_m, group_n);
   else
-    hipLaunchKernelGGL((lmhead_bf16_mfma<BN, BM, WN, WM, false>), grid, dim3(kBlock), 0, st, x,
-                       m, k, w, n, out, ld, col_off, tiles_n, tiles_m);
+    hipLaunchKernelGGL((lmhead_bf16_mfma<C, false>), grid, dim3(C::NT), 0, st, x, m, k, w, n,
+                       out, ld, col_off, tiles_n, tiles_m, group_n);
   return 0;
 }
 
@@ -329,19 +511,27 @@ int launch_lmhead(const void *x, int64_t m, int64_t k, const void *w, int64_t n,
   const uint16_t *xb = static_cast<const uint16_t *>(x);
   const uint16_t *wb = static_cast<const uint16_t *>(w);
   uint16_t *ob = static_cast<uint16_t *>(logits);
+  // Tile shapes by the number of hidden rows M (measured on MI355X):
+  //  - M <= 64 (decode-size batches): the LM head streams W once and is
+  //    bound by HBM; narrow tiles of 128 vocabulary rows keep ~1200 tiles
+  //    in flight and four LDS stages keep W loads well ahead of the MFMAs;
+  //  - M <= 256: 160 vocabulary rows per tile (475 tiles for a 75968-row
+  //    shard, under two rounds over 256 CUs) with 32-wide K stages;
+  //  - larger M is a dense contraction: 256 x 256 tiles over 8 waves, two
+  //    LDS stages, tiles grouped 4 W blocks wide for L2 reuse.
   int rc;
   if (m <= 16)
-    rc = launch_bf16_cfg<256, 16, 4, 1>(xb, m, k, wb, n, ob, ld, col_offset, st);
+    rc = launch_bf16_cfg<Cfg<128, 16, 4, 1, 64, 1, 0, 0, 2, 4>>(xb, m, k, wb, n, ob, ld, col_offset, st);
   else if (m <= 32)
-    rc = launch_bf16_cfg<256, 32, 4, 1>(xb, m, k, wb, n, ob, ld, col_offset, st);
+    rc = launch_bf16_cfg<Cfg<128, 32, 4, 1, 64, 1, 0, 0, 2, 4>>(xb, m, k, wb, n, ob, ld, col_offset, st);
   else if (m <= 64)
-    rc = launch_bf16_cfg<256, 64, 4, 1>(xb, m, k, wb, n, ob, ld, col_offset, st);
+    rc = launch_bf16_cfg<Cfg<128, 64, 4, 1, 64, 1, 0, 0, 2, 4>>(xb, m, k, wb, n, ob, ld, col_offset, st);
   else if (m <= 128)
-    rc = launch_bf16_cfg<256, 128, 2, 2>(xb, m, k, wb, n, ob, ld, col_offset, st);
+    rc = launch_bf16_cfg<Cfg<256, 128, 4, 2, 64, 1, 0, 0, 2, 3>>(xb, m, k, wb, n, ob, ld, col_offset, st, 4);
   else if (m <= 256)
-    rc = launch_bf16_cfg<128, 256, 2, 2>(xb, m, k, wb, n, ob, ld, col_offset, st);
+    rc = launch_bf16_cfg<Cfg<160, 256, 2, 4, 32, 1, 0, 0, 2, 5>>(xb, m, k, wb, n, ob, ld, col_offset, st);
   else
-    rc = launch_bf16_cfg<256, 256, 2, 2>(xb, m, k, wb, n, ob, ld, col_offset, st);
+    rc = launch_bf16_cfg<Cfg<256, 256, 2, 4, 64, 1, 0, 0, 2, 2>>(xb, m, k, wb, n, ob, ld, col_offset, st, 4);
   if (rc != 0) return rc;
   return static_cast<int>(hipGetLastError());
 }

@@ -98,6 +98,8 @@ vpe_status vpe_lmhead(const void *x, int64_t m, int64_t dim, const void *weight,
   // the grid's second dimension counts blocks of at least 64 rows of X and
   // must stay below 65536
   if (m > (int64_t(1) << 21)) return VPE_ERR_SHAPE;
+  // a tile's rows are addressed with 32-bit byte offsets
+  if (dim > (int64_t(1) << 20)) return VPE_ERR_SHAPE;
   if (col_offset < 0 || ld_out < 1 || shard_rows > ld_out - col_offset) return VPE_ERR_RANGE;
   if (m > kMaxElems / ld_out) return VPE_ERR_SHAPE;
   if (m == 0) return VPE_OK;
