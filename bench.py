@@ -53,6 +53,24 @@ def parse_args():
     return p.parse_args()
 
 
+def recorded_traffic(workload: str, kind: str):
+    """HBM bytes per dispatch recorded by hardware counters (profiles/traffic.json),
+    or None when none were recorded or the kernel source changed since."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        with open(path) as f:
+            rec = json.load(f)
+        k = rec["kernels"][f"{workload}/{kind}"]
+        with open(os.path.join(ROOT, k["source"]), "rb") as f:
+            if hashlib.sha256(f.read()).hexdigest() != k["source_sha256"]:
+                return None
+        cp = rec["copy_probe"]
+        return int((k["fetch_kib"] * cp["fetch_scale"] + k["write_kib"] * cp["write_scale"]) * 1024)
+    except (OSError, KeyError, ValueError):
+        return None
+
+
 def algorithmic_bytes(w, ids, ranks_owned):
     """Bytes the method must move per step, by kernel kind."""
     s = w.elem_bytes
@@ -251,6 +269,9 @@ def main():
                 "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": None,
                 "algorithmic_bytes_per_launch": dom_bytes}
     roof["avg_launch_us"] = round(dom_us, 3)
+    roof["traffic"] = recorded_traffic(w.name, dom)
+    for kind in breakdown:
+        breakdown[kind]["hbm_bytes_counted"] = recorded_traffic(w.name, kind)
 
     # ---------------- CPU baseline: the oracle on the same workload ----------------
     cpu = None
