@@ -154,8 +154,14 @@ void launch_gather_chunk(Index index, int64_t n_rows, const V *s, V *d, int64_t 
     hipLaunchKernelGGL((gather_rows_wide<V, VPL, RPW, Index>), grid, dim3(kBlock), 0, stream, \
                        index, n_rows, s, d, vr);                                             \
   } while (0)
-    if (vpl <= 2) VPE_WIDE(2, 4);
-    else if (vpl <= 4) VPE_WIDE(4, 2);
+    // Several rows per wave put more bytes in flight per wave, but only pay
+    // when the grid still has enough waves to fill the chip (8 per SIMD over
+    // 256 CUs); short gathers take one row per wave.
+    const bool many = n_rows >= int64_t(4) * 8 * 4 * 256;
+    if (vpl <= 2 && many) VPE_WIDE(2, 4);
+    else if (vpl <= 2) VPE_WIDE(2, 1);
+    else if (vpl <= 4 && many) VPE_WIDE(4, 2);
+    else if (vpl <= 4) VPE_WIDE(4, 1);
     else VPE_WIDE(8, 1);
 #undef VPE_WIDE
   }

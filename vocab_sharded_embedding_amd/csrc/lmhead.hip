@@ -42,16 +42,24 @@ __device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
 }
 
 // ---------------------------------------------------------------------------
-// LDS tile layout: a row holds BK bf16 = BK/8 pieces of 16 bytes.  Piece p of
-// row r is stored at slot p ^ f(r), f(r) = r mod P (SWZ 0) or (r/2) mod P
-// (SWZ 1), P = BK/8: the 16 rows one MFMA fragment reads at the same k then
-// fall in different LDS banks.
+// LDS tile layout: a row holds BK bf16 = P = BK/8 pieces of 16 bytes.  The LDS
+// serves a 16-byte read in passes of 8 lanes over 32 four-byte banks (128
+// bytes), and the 8 lanes of a pass read the same piece of 8 consecutive
+// rows.  Piece p of row r is stored at slot p ^ f(r) with
+//   f(r) = (r / G) mod P,   G = rows per 128 bytes (2 for BK = 32, else 1),
+// so those 8 rows' pieces land in 8 distinct 16-byte bank groups
+// (SWZ 1: f(r) = (r / 2) mod P for every BK, kept for measurements).
 // ---------------------------------------------------------------------------
 template <int BK, int SWZ>
-__device__ __forceinline__ int lds_piece_offset(int row, int piece) {
+__device__ __forceinline__ int lds_swizzle(int row) {
   constexpr int P = BK / 8;
-  const int f = (SWZ == 0) ? (row & (P - 1)) : ((row >> 1) & (P - 1));
-  return row * BK + ((piece ^ f) << 3);  // in bf16 elements
+  constexpr int G = (SWZ == 1) ? 2 : ((BK * 2 >= 128) ? 1 : 128 / (BK * 2));
+  return (row / G) & (P - 1);
+}
+
+template <int BK, int SWZ>
+__device__ __forceinline__ int lds_piece_offset(int row, int piece) {
+  return row * BK + ((piece ^ lds_swizzle<BK, SWZ>(row)) << 3);  // in bf16 elements
 }
 
 // Workgroup tile order.  Work-groups are handed to the 8 XCDs round-robin
@@ -266,7 +274,7 @@ __global__ __launch_bounds__(C::NT) void lmhead_bf16_mfma(
       for (int p = 0; p < kPPT; ++p) {
         const int row0 = p * kRowsPerPass + wave_u * kRowsPerWaveLoad;  // wave-uniform
         const int row = row0 + lrow;
-        const int piece = lslot ^ ((SWZ == 0) ? (row & (kPieces - 1)) : ((row >> 1) & (kPieces - 1)));
+        const int piece = lslot ^ lds_swizzle<BK, SWZ>(row);
         bool in_w;
         if constexpr (BN % kRowsPerPass == 0) in_w = p * kRowsPerPass < BN;
         else in_w = row0 < BN;
@@ -516,7 +524,7 @@ int launch_lmhead(const void *x, int64_t m, int64_t k, const void *w, int64_t n,
   //    bound by HBM; narrow tiles of 128 vocabulary rows keep ~1200 tiles
   //    in flight and four LDS stages keep W loads well ahead of the MFMAs;
   //  - M <= 256: 160 vocabulary rows per tile (475 tiles for a 75968-row
-  //    shard, under two rounds over 256 CUs) with 32-wide K stages;
+  //    shard, under two rounds over 256 CUs), two LDS stages;
   //  - larger M is a dense contraction: 256 x 256 tiles over 8 waves, two
   //    LDS stages, tiles grouped 4 W blocks wide for L2 reuse.
   int rc;
@@ -529,7 +537,7 @@ int launch_lmhead(const void *x, int64_t m, int64_t k, const void *w, int64_t n,
   else if (m <= 128)
     rc = launch_bf16_cfg<Cfg<256, 128, 4, 2, 64, 1, 0, 0, 2, 3>>(xb, m, k, wb, n, ob, ld, col_offset, st, 4);
   else if (m <= 256)
-    rc = launch_bf16_cfg<Cfg<160, 256, 2, 4, 32, 1, 0, 0, 2, 5>>(xb, m, k, wb, n, ob, ld, col_offset, st);
+    rc = launch_bf16_cfg<Cfg<160, 256, 2, 4, 64, 1, 0, 0, 2, 2>>(xb, m, k, wb, n, ob, ld, col_offset, st);
   else
     rc = launch_bf16_cfg<Cfg<256, 256, 2, 4, 64, 1, 0, 0, 2, 2>>(xb, m, k, wb, n, ob, ld, col_offset, st, 4);
   if (rc != 0) return rc;
