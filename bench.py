@@ -47,6 +47,12 @@ def parse_args():
                    help="input copies to rotate through (0 = enough for >= 1 GiB)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-threads", type=int, default=0, help="0 = min(16, cores available)")
+    p.add_argument("--unfused-prefill", action="store_true",
+                   help="prefill workloads: separate last-position select + LM head instead of "
+                        "the LM head that reads the last positions itself")
+    p.add_argument("--argmax", action="store_true",
+                   help="LM head reduced on the fly to each row's greedy pick (largest logit "
+                        "and its id) instead of storing the logits")
     p.add_argument("--copy-probe-mib", type=int, default=0,
                    help="after timing, run one device-to-device copy of this many MiB "
                         "(a reference kernel for hardware byte counters)")
@@ -71,7 +77,7 @@ def recorded_traffic(workload: str, kind: str):
         return None
 
 
-def algorithmic_bytes(w, ids, ranks_owned):
+def algorithmic_bytes(w, ids, ranks_owned, fused_prefill=False, argmax=False):
     """Bytes the method must move per step, by kernel kind."""
     s = w.elem_bytes
     D = w.dim
@@ -82,12 +88,20 @@ def algorithmic_bytes(w, ids, ranks_owned):
     out["embed"] = [n * idb + n * D * s + h * D * s for h in ranks_owned]
     if len(w.ranks) > 1:
         out["sum"] = [(len(w.ranks) + 1) * n * D * s]
-    if w.seqs:
+    if w.seqs and not fused_prefill:
         out["select"] = [w.seqs * (4 + 2 * D * s)]
     M = w.lm_rows
     R = w.shard_rows
-    out["lmhead"] = [M * D * s + R * D * s + M * R * s for _ in w.ranks]
-    flops = {"lmhead": [2 * M * R * D for _ in w.ranks]}
+    if argmax:
+        # keys: 8 bytes per row written by the init, folded by every shard,
+        # read by the decode, which writes 4 + 8 bytes per row
+        out["argmax_init"] = [M * 8]
+        out["lmhead_argmax"] = [M * D * s + R * D * s + M * 8 for _ in w.ranks]
+        out["argmax_decode"] = [M * (8 + 12)]
+        flops = {"lmhead_argmax": [2 * M * R * D for _ in w.ranks]}
+    else:
+        out["lmhead"] = [M * D * s + R * D * s + M * R * s for _ in w.ranks]
+        flops = {"lmhead": [2 * M * R * D for _ in w.ranks]}
     return out, flops
 
 
@@ -137,7 +151,7 @@ def main():
     M = w.lm_rows
     per_copy = (sum(a.nbytes for a in shards_h.values()) + ids_h.nbytes + hidden_h.nbytes
                 + len(w.ranks) * ids_h.size * w.dim * s
-                + M * (w.vocab if w.concat else w.shard_rows) * s)
+                + (M * 28 if args.argmax else M * (w.vocab if w.concat else w.shard_rows) * s))
     copies = args.copies or max(1, -(-CACHE_DEFEAT_BYTES // per_copy))
     base = {"ids": up(ids_h), "hidden": up(hidden_h),
             "cu": up(cu_h) if cu_h is not None else None,
@@ -153,8 +167,13 @@ def main():
                           if len(w.ranks) > 1 else d["partials"][0])
         d["x"] = (torch.empty((w.seqs, w.dim), dtype=tdt, device=dev) if w.seqs
                   else d["hidden"])
-        d["logits"] = torch.empty((M, w.vocab if w.concat else w.shard_rows), dtype=tdt,
-                                  device=dev)
+        if args.argmax:
+            d["best"] = torch.empty(M, dtype=torch.int64, device=dev)
+            d["pick_val"] = torch.empty(M, dtype=torch.float32, device=dev)
+            d["pick_tok"] = torch.empty(M, dtype=torch.int64, device=dev)
+        else:
+            d["logits"] = torch.empty((M, w.vocab if w.concat else w.shard_rows), dtype=tdt,
+                                      device=dev)
         sets.append(d)
     del base
     torch.cuda.synchronize()
@@ -179,15 +198,34 @@ def main():
             seq.append(("sum", lib.vpe_sum_partials,
                         (arr, len(w.ranks), ids_h.size * w.dim, dcode, d["embed_out"].data_ptr(),
                          sh)))
-        if w.seqs:
+        fused = bool(w.seqs) and not args.unfused_prefill and not args.argmax
+        if w.seqs and not fused:
             seq.append(("select", lib.vpe_last_token_select,
                         (d["hidden"].data_ptr(), hidden_h.shape[0], w.dim, dcode,
                          d["cu"].data_ptr(), w.seqs, d["x"].data_ptr(), sh)))
+        if args.argmax:
+            seq.append(("argmax_init", lib.vpe_argmax_init, (d["best"].data_ptr(), M, sh)))
         for r in w.ranks:
-            seq.append(("lmhead", lib.vpe_lmhead,
-                        (d["x"].data_ptr(), M, w.dim, d["shards"][r].data_ptr(), w.shard_rows,
-                         dcode, d["logits"].data_ptr(), d["logits"].shape[1],
-                         w.rank_start(r) if w.concat else 0, sh)))
+            if args.argmax:
+                seq.append(("lmhead_argmax", lib.vpe_lmhead_argmax,
+                            (d["x"].data_ptr(), M, w.dim, d["shards"][r].data_ptr(), w.shard_rows,
+                             dcode, w.rank_start(r), d["best"].data_ptr(), sh)))
+            elif fused:
+                # the LM head reads each sequence's last position itself
+                seq.append(("lmhead", lib.vpe_lmhead_prefill,
+                            (d["hidden"].data_ptr(), hidden_h.shape[0], w.dim, d["cu"].data_ptr(),
+                             w.seqs, d["shards"][r].data_ptr(), w.shard_rows, dcode,
+                             d["logits"].data_ptr(), d["logits"].shape[1],
+                             w.rank_start(r) if w.concat else 0, sh)))
+            else:
+                seq.append(("lmhead", lib.vpe_lmhead,
+                            (d["x"].data_ptr(), M, w.dim, d["shards"][r].data_ptr(), w.shard_rows,
+                             dcode, d["logits"].data_ptr(), d["logits"].shape[1],
+                             w.rank_start(r) if w.concat else 0, sh)))
+        if args.argmax:
+            seq.append(("argmax_decode", lib.vpe_argmax_decode,
+                        (d["best"].data_ptr(), M, d["pick_val"].data_ptr(),
+                         d["pick_tok"].data_ptr(), sh)))
         calls.append(seq)
 
     def run_step(k, events=None):
@@ -227,7 +265,9 @@ def main():
         ms = [evs[k][j][0].elapsed_time(evs[k][j][1]) for k in range(args.steps)]
         per_kind_ms.setdefault(kind, []).append(float(np.mean(ms)))
 
-    bytes_, flops_ = algorithmic_bytes(w, ids_h, owned)
+    fused_prefill = bool(w.seqs) and not args.unfused_prefill and not args.argmax
+    bytes_, flops_ = algorithmic_bytes(w, ids_h, owned, fused_prefill=fused_prefill,
+                                       argmax=args.argmax)
     step_bytes = sum(sum(v) for v in bytes_.values())
     ms_per_step = t_total * 1e3 / args.steps
     value = step_bytes / (ms_per_step * 1e-3) / 1e9
@@ -242,8 +282,8 @@ def main():
              "hbm_frac": [round(g / HBM_PEAK_GBS, 4) for g in gbs]}
         if kind == "embed":
             e["rows_per_s"] = [round(ids_h.size / (u * 1e-6), 1) for u in us]
-        if kind == "lmhead":
-            f = flops_["lmhead"]
+        if kind in flops_:
+            f = flops_[kind]
             tf = [ff / (u * 1e-6) / 1e12 for ff, u in zip(f, us)]
             e["TFLOP_per_s"] = [round(t, 2) for t in tf]
             peak = BF16_MFMA_PEAK_TFLOPS if w.dtype == "bf16" else FP32_VECTOR_PEAK_TFLOPS
@@ -257,7 +297,7 @@ def main():
     dom_flops = float(np.mean(flops_.get(dom, [0])))
     ai = dom_flops / dom_bytes if dom_bytes else 0.0
     ridge = (BF16_MFMA_PEAK_TFLOPS * 1e12) / (HBM_PEAK_GBS * 1e9)
-    if dom == "lmhead" and ai > ridge:
+    if dom in flops_ and ai > ridge:
         ach = dom_flops / (dom_us * 1e-6) / 1e12
         roof = {"kernel": dom, "bound": "mfma", "achieved": round(ach, 2),
                 "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
@@ -286,6 +326,9 @@ def main():
         "config": {"workload": w.name, "vocab": w.vocab, "dim": w.dim, "tp": w.tp,
                    "ranks": list(w.ranks), "n_ids": int(ids_h.size), "id_dist": w.id_dist,
                    "lm_rows": M, "seqs": w.seqs, "concat": w.concat, "rotating_copies": copies,
+                   "prefill_select": ("fused" if fused_prefill else "separate")
+                   if w.seqs else None,
+                   "lm_output": "argmax" if args.argmax else "logits",
                    "step_algorithmic_bytes": step_bytes},
         "roofline": roof,
         "cpu_baseline": cpu,

@@ -173,6 +173,83 @@ vpe_status vpe_lmhead(const void *x, int64_t m, int64_t dim, const void *weight,
                       int64_t shard_rows, vpe_dtype dt, void *logits, int64_t ld_out,
                       int64_t col_offset, void *stream);
 
+/*
+ * Prefill LM head with the last-position select folded in: the logits of the
+ * last position of every packed sequence, read straight out of the prefill
+ * activations ([Guide-3.3] section 6: only the last position of each
+ * sequence is projected; [TP-vocab] sections 4 and 6 for the shard product
+ * and its column offset).  Equal to vpe_last_token_select followed by
+ * vpe_lmhead, without the [n_seqs, dim] intermediate or its launch:
+ *
+ *   logits[s * ld_out + col_offset + j] = sum_k hidden[cu_seqlens[s+1]-1, k] * weight[j, k]
+ *
+ * hidden      device, [n_tokens, dim] of `dt`.
+ * cu_seqlens  device, int32 [n_seqs + 1] (same precondition as
+ *             vpe_last_token_select; a sequence whose last index falls
+ *             outside [0, n_tokens) gets all-zero logits, nothing is read).
+ * weight, logits, ld_out, col_offset, accumulation and rounding: as vpe_lmhead.
+ * n_seqs == 0 is a no-op.
+ * Errors: VPE_ERR_NULL, VPE_ERR_SHAPE (n_tokens < 0 or >= 2^31, n_seqs < 0
+ * or > 2^21, dim < 1 or > 2^20, shard_rows < 1), VPE_ERR_RANGE,
+ * VPE_ERR_DTYPE, VPE_ERR_ALIGN.
+ */
+vpe_status vpe_lmhead_prefill(const void *hidden, int64_t n_tokens, int64_t dim,
+                              const int32_t *cu_seqlens, int64_t n_seqs, const void *weight,
+                              int64_t shard_rows, vpe_dtype dt, void *logits, int64_t ld_out,
+                              int64_t col_offset, void *stream);
+
+/*
+ * Greedy pick over the vocabulary without materialising the logits.  The
+ * full-vocabulary logits exist to feed the sampler ([TP-vocab] section 4:
+ * each rank's shard of the logits is gathered and concatenated; [Guide-3.3]
+ * section 6); for greedy sampling each rank can instead reduce its shard to
+ * (largest logit, its id) and the ranks combine those.  Here one 64-bit key
+ * per row holds the running pick:
+ *
+ *   key = (order(v) << 32) | (0xFFFFFFFF - id)
+ *
+ * (order() maps binary32 bits to an unsigned integer ordered like the
+ * values), so the largest key is the largest logit and, among equal logits,
+ * the smallest id: the first maximum of the concatenated row.  Shards fold
+ * their candidates in with atomic max, so calling vpe_lmhead_argmax for every
+ * rank's shard on the same `best` is the combine.
+ *
+ * Sequence: vpe_argmax_init(best) once; vpe_lmhead_argmax(...) per shard;
+ * vpe_argmax_decode(best) -> (max logit, token id) per row.  All on streams
+ * ordered by the caller; concurrent shard calls on one `best` are fine (the
+ * fold is an atomic max).
+ *
+ * The logit compared is the one vpe_lmhead would store: fp32 accumulation
+ * rounded to `dt` (round to nearest even), widened back to fp32.
+ */
+
+/* best: device uint64 [m], m <= 2^21; sets every key to 0 (below every real
+ * logit).  Errors: VPE_ERR_SHAPE, VPE_ERR_NULL, VPE_ERR_ALIGN (best not
+ * 8-byte aligned). */
+vpe_status vpe_argmax_init(uint64_t *best, int64_t m, void *stream);
+
+/*
+ * Folds one shard's logits x . weight^T into best[m]: for each row i the
+ * largest logit over the shard's rows j, with id vocab_start + j.
+ * x, weight, dt, dim, shard_rows: as vpe_lmhead.  best: device uint64 [m],
+ * initialised by vpe_argmax_init.  m == 0 is a no-op.
+ * Errors: VPE_ERR_NULL, VPE_ERR_SHAPE (m < 0 or > 2^21, dim < 1 or > 2^20,
+ * shard_rows < 1), VPE_ERR_RANGE (vocab_start < 0 or vocab_start +
+ * shard_rows >= 2^32), VPE_ERR_DTYPE, VPE_ERR_ALIGN.
+ */
+vpe_status vpe_lmhead_argmax(const void *x, int64_t m, int64_t dim, const void *weight,
+                             int64_t shard_rows, vpe_dtype dt, int64_t vocab_start,
+                             uint64_t *best, void *stream);
+
+/*
+ * max_logit[i] (device float [m], may be NULL) and token[i] (device int64
+ * [m], may be NULL, not both) decoded from best[i], m <= 2^21.  A row no
+ * shard folded into decodes to (NaN with the sign bit set, 0xFFFFFFFF).
+ * Errors: VPE_ERR_SHAPE, VPE_ERR_NULL, VPE_ERR_ALIGN.
+ */
+vpe_status vpe_argmax_decode(const uint64_t *best, int64_t m, float *max_logit, int64_t *token,
+                             void *stream);
+
 /* Static, NUL-terminated name of a status code ("VPE_OK", ...). */
 const char *vpe_status_string(vpe_status s);
 

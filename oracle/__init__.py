@@ -62,6 +62,8 @@ def _load():
         lib.orc_last_token_select.argtypes = [vp, i64, i64, ci, vp, i64, vp]
         lib.orc_lmhead_f64.argtypes = [vp, i64, i64, vp, i64, ci, vp, i64, i64, ci]
         lib.orc_logit_f64.argtypes = [vp, i64, vp, ci, i64, i64]
+        lib.orc_argmax_rows.argtypes = [vp, i64, i64, i64, vp, vp]
+        lib.orc_argmax_rows.restype = ci
         lib.orc_logit_f64.restype = ctypes.c_double
         lib.orc_round_bf16.argtypes = [ctypes.c_float]
         lib.orc_round_bf16.restype = ctypes.c_uint16
@@ -191,6 +193,16 @@ def logit_f64(x: np.ndarray, weight: np.ndarray, m: int, j: int) -> float:
     x = np.ascontiguousarray(x)
     weight = np.ascontiguousarray(weight)
     return _load().orc_logit_f64(_ptr(x), x.shape[1], _ptr(weight), _dtype_code(x), m, j)
+
+
+def argmax_rows(logits: np.ndarray):
+    """(max value, first column holding it) of every row of an fp64 [m, n] array."""
+    logits = np.ascontiguousarray(logits, dtype=np.float64)
+    m, n = logits.shape
+    mx = np.empty(m, dtype=np.float64)
+    idx = np.empty(m, dtype=np.int64)
+    _check(_load().orc_argmax_rows(_ptr(logits), m, n, n, _ptr(mx), _ptr(idx)), "argmax_rows")
+    return mx, idx
 
 
 def round_bf16(values) -> np.ndarray:

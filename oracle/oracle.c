@@ -272,6 +272,28 @@ int orc_lmhead_f64(const void *x, int64_t m, int64_t dim, const void *weight,
     return ORC_OK;
 }
 
+/* ------------------------------------------------------------------ */
+/* greedy pick over the concatenated logits ([TP-vocab] section 4: the  */
+/* full-vocabulary logits feed the sampler; the first maximum wins, as */
+/* an argmax over a row does): for each row m of a [m_rows, ld] fp64   */
+/* buffer, the largest value in columns [0, n_cols) and its column.     */
+/* ------------------------------------------------------------------ */
+int orc_argmax_rows(const double *logits, int64_t m_rows, int64_t n_cols, int64_t ld,
+                    double *max_out, int64_t *idx_out) {
+    if (m_rows < 0 || n_cols < 1 || ld < n_cols) return ORC_ERR_ARG;
+    if (m_rows == 0) return ORC_OK;
+    if (!logits || !max_out || !idx_out) return ORC_ERR_ARG;
+    for (int64_t m = 0; m < m_rows; ++m) {
+        const double *row = logits + m * ld;
+        int64_t best = 0;
+        for (int64_t j = 1; j < n_cols; ++j)
+            if (row[j] > row[best]) best = j;
+        max_out[m] = row[best];
+        idx_out[m] = best;
+    }
+    return ORC_OK;
+}
+
 /* single logit, for sampled checks at sizes the full product would take too long */
 double orc_logit_f64(const void *x, int64_t dim, const void *weight, int dtype,
                      int64_t m, int64_t j) {

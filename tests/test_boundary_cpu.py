@@ -22,9 +22,11 @@ def _declared():
     return sorted(set(re.findall(r"^\s*(?:vpe_status|const char \*)\s*(vpe_\w+)\s*\(", text, re.M)))
 
 
-def test_header_declares_the_five_calls():
+def test_header_declares_the_calls():
     assert _declared() == sorted(["vpe_shard_range", "vpe_embed", "vpe_sum_partials",
-                                  "vpe_last_token_select", "vpe_lmhead", "vpe_status_string"])
+                                  "vpe_last_token_select", "vpe_lmhead", "vpe_lmhead_prefill",
+                                  "vpe_argmax_init", "vpe_lmhead_argmax", "vpe_argmax_decode",
+                                  "vpe_status_string"])
 
 
 def test_library_exports_every_declared_symbol():
@@ -157,3 +159,56 @@ def test_product_package_does_not_import_the_oracle():
                 text = open(os.path.join(dirpath, fn), encoding="utf-8").read()
                 for bad in ("import oracle", "from oracle", "liboracle", "oracle.c"):
                     assert bad not in text, (fn, bad)
+
+
+def test_lmhead_prefill_validation():
+    lib = vpe.load_library()
+    ok = dict(h=FAKE, t=100, dim=64, cu=FAKE, s=4, w=FAKE, rows=100, dt=BF16, out=FAKE, ld=100,
+              col=0)
+
+    def call(**kw):
+        a = {**ok, **kw}
+        return lib.vpe_lmhead_prefill(a["h"], a["t"], a["dim"], a["cu"], a["s"], a["w"],
+                                      a["rows"], a["dt"], a["out"], a["ld"], a["col"], None)
+
+    assert call(dt=5) == vpe.VPE_ERR_DTYPE
+    assert call(t=-1) == vpe.VPE_ERR_SHAPE
+    assert call(t=2 ** 31) == vpe.VPE_ERR_SHAPE
+    assert call(s=-1) == vpe.VPE_ERR_SHAPE
+    assert call(s=2 ** 21 + 1) == vpe.VPE_ERR_SHAPE
+    assert call(dim=0) == vpe.VPE_ERR_SHAPE
+    assert call(dim=2 ** 20 + 8) == vpe.VPE_ERR_SHAPE
+    assert call(rows=0) == vpe.VPE_ERR_SHAPE
+    assert call(ld=99) == vpe.VPE_ERR_RANGE
+    assert call(col=1) == vpe.VPE_ERR_RANGE
+    assert call(cu=None) == vpe.VPE_ERR_NULL
+    assert call(h=None) == vpe.VPE_ERR_NULL
+    assert call(cu=FAKE + 2) == vpe.VPE_ERR_ALIGN
+    assert call(dt=F32, h=FAKE + 2) == vpe.VPE_ERR_ALIGN
+    assert call(s=0, h=None, cu=None, w=None, out=None) == vpe.VPE_OK
+
+
+def test_argmax_validation():
+    lib = vpe.load_library()
+    assert lib.vpe_argmax_init(FAKE, -1, None) == vpe.VPE_ERR_SHAPE
+    assert lib.vpe_argmax_init(None, 4, None) == vpe.VPE_ERR_NULL
+    assert lib.vpe_argmax_init(FAKE + 4, 4, None) == vpe.VPE_ERR_ALIGN
+    assert lib.vpe_argmax_init(None, 0, None) == vpe.VPE_OK
+    f = lib.vpe_lmhead_argmax
+    assert f(FAKE, 4, 64, FAKE, 100, 9, 0, FAKE, None) == vpe.VPE_ERR_DTYPE
+    assert f(FAKE, -1, 64, FAKE, 100, BF16, 0, FAKE, None) == vpe.VPE_ERR_SHAPE
+    assert f(FAKE, 4, 0, FAKE, 100, BF16, 0, FAKE, None) == vpe.VPE_ERR_SHAPE
+    assert f(FAKE, 4, 64, FAKE, 0, BF16, 0, FAKE, None) == vpe.VPE_ERR_SHAPE
+    assert f(FAKE, 4, 64, FAKE, 100, BF16, -1, FAKE, None) == vpe.VPE_ERR_RANGE
+    assert f(FAKE, 4, 64, FAKE, 100, BF16, 2 ** 32 - 100, FAKE, None) == vpe.VPE_ERR_RANGE
+    assert f(FAKE, 4, 64, FAKE, 100, BF16, 0, None, None) == vpe.VPE_ERR_NULL
+    assert f(FAKE, 4, 64, FAKE, 100, BF16, 0, FAKE + 4, None) == vpe.VPE_ERR_ALIGN
+    assert f(None, 0, 64, None, 100, BF16, 0, None, None) == vpe.VPE_OK
+    d = lib.vpe_argmax_decode
+    assert d(FAKE, 4, None, None, None) == vpe.VPE_ERR_NULL
+    assert d(FAKE, -1, FAKE, FAKE, None) == vpe.VPE_ERR_SHAPE
+    assert d(FAKE, 4, FAKE + 2, FAKE, None) == vpe.VPE_ERR_ALIGN
+    assert d(None, 0, None, None, None) == vpe.VPE_OK
+    assert lib.vpe_argmax_init(FAKE, 2 ** 21 + 1, None) == vpe.VPE_ERR_SHAPE
+    assert d(FAKE, 2 ** 21 + 1, FAKE, FAKE, None) == vpe.VPE_ERR_SHAPE
+    assert f(FAKE, 2 ** 21 + 1, 64, FAKE, 100, BF16, 0, FAKE, None) == vpe.VPE_ERR_SHAPE

@@ -336,3 +336,209 @@ def test_binding_rejects_bad_arguments():
     with pytest.raises(vpe.VpeError) as e:
         vpe.vpe_shard_range(151936, 3, 0)
     assert e.value.status == vpe.VPE_ERR_SHARD
+
+
+# ---------------------------------------------------------------------------
+# prefill LM head with the last-position select folded in
+# ---------------------------------------------------------------------------
+def test_lmhead_prefill_workload():
+    d = _inputs("qwen3_0p6b_tp1_prefill")
+    w = d["w"]
+    _say(f"lmhead_prefill {w.name}: T={d['hidden'].shape[0]} S={w.seqs} rows={w.shard_rows}")
+    H = to_dev(d["hidden"])
+    cu = to_dev(d["cu"])
+    Wd = to_dev(d["shards"][0])
+    got_t = vpe.vpe_lmhead_prefill(H, cu, Wd)
+    unfused = vpe.vpe_lmhead(vpe.vpe_last_token_select(H, cu), Wd)
+    got = to_host(got_t)
+    # same tiles, same k order: the fused call is the composition, bit for bit
+    assert got.tobytes() == to_host(unfused).tobytes()
+    ref = oracle.lmhead_f64(oracle.last_token_select(d["hidden"], d["cu"]), d["shards"][0],
+                            nthreads=oracle_threads())
+    assert_logits_close(got, ref, "lmhead_prefill qwen3 prefill")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("seqs,dim,rows", [(1, 64, 100), (7, 200, 333), (37, 1024, 1000),
+                                          (130, 96, 700), (300, 72, 515)])
+def test_lmhead_prefill_ragged(dtype, seqs, dim, rows):
+    cu = wl.cu_seqlens_ragged(200 + seqs, seqs, 1, 40)
+    H = wl.hidden_states(201 + seqs, int(cu[-1]), dim, dtype)
+    W = wl.table_rows(202 + seqs, rows, dim, dtype, 0, rows, std=0.5)
+    ld, col = rows + 9, 5
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    logits = torch.full((seqs, ld), -1536.0, dtype=tdt, device=dev())
+    vpe.vpe_lmhead_prefill(to_dev(H), to_dev(cu), to_dev(W), logits, col_offset=col)
+    got = to_host(logits)
+    ref = oracle.lmhead_f64(oracle.last_token_select(H, cu), W)
+    assert_logits_close(got[:, col:col + rows], ref, f"prefill {dtype} S={seqs} D={dim}")
+    g = as_f64(got)
+    assert np.all(g[:, :col] == -1536.0) and np.all(g[:, col + rows:] == -1536.0)
+
+
+def test_lmhead_prefill_out_of_range_sequence_gives_zero_logits():
+    H = wl.hidden_states(210, 10, 64, "bf16")
+    W = wl.table_rows(211, 50, 64, "bf16", 0, 50, std=0.5)
+    cu = np.array([0, 0, 4, 10, 12], dtype=np.int32)  # empty first sequence; 12 > 10 tokens
+    got = as_f64(to_host(vpe.vpe_lmhead_prefill(to_dev(H), to_dev(cu), to_dev(W))))
+    assert np.all(got[0] == 0) and np.all(got[3] == 0)
+    ref = oracle.lmhead_f64(H[[3, 9]], W)
+    assert_logits_close(got[1:3].astype(np.float64), ref, "prefill valid rows")
+
+
+def test_parallel_lmhead_layer_prefill_and_decode():
+    V, D, tp = 512, 128, 2
+    full = wl.table_rows(220, V, D, "bf16", 0, V)
+    cu = wl.cu_seqlens_ragged(221, 5, 1, 9)
+    H = wl.hidden_states(222, int(cu[-1]), D, "bf16")
+    full_d = to_dev(full).view(torch.bfloat16)
+    logits = torch.empty((5, V), dtype=torch.bfloat16, device=dev())
+    for r in range(tp):
+        head = vpe.ParallelLMHead(V, D, tp_size=tp, tp_rank=r, device=dev())
+        head.weight_loader(head.weight, full_d)
+        head(to_dev(H), cu_seqlens=to_dev(cu), logits=logits)
+    ref = oracle.lmhead_f64(oracle.last_token_select(H, cu), full)
+    assert_logits_close(to_host(logits), ref, "ParallelLMHead prefill")
+    emb = [vpe.VocabParallelEmbedding(V, D, tp_size=tp, tp_rank=r, device=dev()) for r in range(tp)]
+    ids = wl.token_ids(223, V, 77)
+    parts = []
+    for e in emb:
+        e.weight_loader(e.weight, full_d)
+        parts.append(e(to_dev(ids)))
+    total = to_host(vpe.VocabParallelEmbedding.sum_partials(parts))
+    assert total.tobytes() == oracle.embed(ids, full, 0).tobytes()
+
+
+# ---------------------------------------------------------------------------
+# greedy pick over the vocabulary without materialising the logits
+# ---------------------------------------------------------------------------
+def _int_inputs(seed, m, n, k, dtype, lo=-1, hi=1):
+    """Small-integer X and W: every logit is an integer of magnitude <= k, exact
+    in fp32 accumulation and (k <= 256) in bf16, so both sides decide on the
+    same values and equal logits are common."""
+    rng = np.random.default_rng(seed)
+    X = rng.integers(lo, hi + 1, size=(m, k)).astype(np.float32)
+    W = rng.integers(lo, hi + 1, size=(n, k)).astype(np.float32)
+    if dtype == "bf16":
+        X, W = wl.f32_to_bf16_bits(X), wl.f32_to_bf16_bits(W)
+    return X, W
+
+
+def _pick(x_d, shards, starts, order=None):
+    best = torch.empty(x_d.shape[0], dtype=torch.int64, device=dev())
+    vpe.vpe_argmax_init(best)
+    for r in (order if order is not None else range(len(shards))):
+        vpe.vpe_lmhead_argmax(x_d, shards[r], starts[r], best)
+    val, tok = vpe.vpe_argmax_decode(best)
+    return to_host(val).astype(np.float64), to_host(tok)
+
+
+ARGMAX_SHAPES = [(1, 1, 8), (3, 5, 7), (16, 128, 64), (17, 129, 65), (40, 1000, 128),
+                 (64, 777, 256), (100, 515, 96), (257, 1300, 64), (300, 2100, 200)]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("m,n,k", ARGMAX_SHAPES)
+def test_argmax_exact_on_integer_logits(dtype, m, n, k):
+    # integer logits: the oracle's first maximum is the unique right answer
+    X, W = _int_inputs(300 + m + n, m, n, k, dtype)
+    val, tok = _pick(to_dev(X), [to_dev(W)], [0])
+    ref_max, ref_idx = oracle.argmax_rows(oracle.lmhead_f64(X, W))
+    assert np.array_equal(tok, ref_idx), f"{dtype} {m}x{n}x{k}"
+    assert np.array_equal(val, ref_max)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("tp,order", [(2, "forward"), (2, "reverse"), (4, "reverse"), (3, "forward")])
+def test_argmax_shards_combine_to_global_first_maximum(dtype, tp, order):
+    m, V, k = 70, 3001, 64
+    X, W = _int_inputs(330 + tp, m, V, k, dtype, lo=0, hi=1)
+    # plant equal maxima in every shard for a few rows: the smallest id must win
+    per = -(-V // tp)
+    starts = [min(r * per, V) for r in range(tp)]
+    ends = [min((r + 1) * per, V) for r in range(tp)]
+    one = np.float32(1) if dtype == "f32" else wl.f32_to_bf16_bits(np.ones((1, 1), np.float32))[0, 0]
+    for r in range(tp):
+        W[ends[r] - 1, :] = one  # logit = row sum of X, the largest possible
+    x_d = to_dev(X)
+    shards = [to_dev(W[s:e]) for s, e in zip(starts, ends)]
+    seq = list(range(tp)) if order == "forward" else list(reversed(range(tp)))
+    val, tok = _pick(x_d, shards, starts, seq)
+    ref_max, ref_idx = oracle.argmax_rows(oracle.lmhead_f64(X, W))
+    assert np.array_equal(tok, ref_idx) and np.array_equal(val, ref_max)
+    # X >= 0, so shard 0's planted row reaches every row's maximum
+    assert np.all(tok <= ends[0] - 1)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("m,n", [(5, 130), (33, 321), (129, 333)])
+def test_argmax_ignores_padding_columns_when_all_logits_are_negative(dtype, m, n):
+    # every logit < 0: a padded column read as zero would win if it were not excluded
+    X, W = _int_inputs(360 + m, m, n, 64, dtype, lo=1, hi=2)
+    Wn = W ^ np.uint16(0x8000) if dtype == "bf16" else -W
+    val, tok = _pick(to_dev(X), [to_dev(Wn)], [0])
+    ref_max, ref_idx = oracle.argmax_rows(oracle.lmhead_f64(X, Wn))
+    assert np.all(ref_max < 0)
+    assert np.array_equal(tok, ref_idx) and np.array_equal(val, ref_max)
+
+
+def test_argmax_matches_the_stored_logits_bit_for_bit():
+    # the pick is the first maximum of exactly the logits vpe_lmhead stores
+    for m, n, k in [(16, 2000, 1024), (64, 1500, 1024), (100, 1000, 512), (300, 1700, 256)]:
+        X = wl.hidden_states(380 + m, m, k, "bf16")
+        W = wl.table_rows(381 + m, n, k, "bf16", 0, n, std=0.5)
+        x_d, w_d = to_dev(X), to_dev(W)
+        stored = as_f64(to_host(vpe.vpe_lmhead(x_d, w_d)))
+        val, tok = _pick(x_d, [w_d], [1000])
+        assert np.array_equal(tok - 1000, np.argmax(stored, axis=1)), f"{m}x{n}x{k}"
+        assert np.array_equal(val, stored.max(axis=1))
+
+
+@pytest.mark.parametrize("name", ["qwen3_0p6b_tp2_rank0", "qwen3_0p6b_tp2_all_ranks"])
+def test_argmax_workload_is_a_valid_greedy_pick(name):
+    d = _inputs(name)
+    w = d["w"]
+    _say(f"argmax {name}: M={w.lm_rows} ranks={list(w.ranks)} rows={w.shard_rows}")
+    x_h = _lm_rows(d)
+    x_d = to_dev(x_h)
+    shards = [to_dev(d["shards"][r]) for r in w.ranks]
+    starts = [w.rank_start(r) for r in w.ranks]
+    val, tok = _pick(x_d, shards, starts, list(reversed(range(len(shards)))))
+    # against the logits the library stores: exact
+    stored = np.full((x_h.shape[0], w.vocab), -np.inf)
+    for s, wd in zip(starts, shards):
+        stored[:, s:s + w.shard_rows] = as_f64(to_host(vpe.vpe_lmhead(x_d, wd)))
+    assert np.array_equal(tok, np.argmax(stored, axis=1))
+    assert np.array_equal(val, stored.max(axis=1))
+    # against the oracle on sampled rows: the pick's fp64 logit is within the
+    # logit tolerance of the fp64 maximum, and the reported value within
+    # tolerance of the pick's fp64 logit
+    rng = np.random.default_rng(7)
+    M = x_h.shape[0]
+    nt = oracle_threads()
+    for m in sorted({0, M - 1, *rng.integers(0, M, size=6).tolist()}):
+        ref = np.full((1, w.vocab), -np.inf)
+        for r, s in zip(w.ranks, starts):
+            ref[:, s:s + w.shard_rows] = oracle.lmhead_f64(x_h[m:m + 1], d["shards"][r],
+                                                           nthreads=nt)
+        ref_max, _ = oracle.argmax_rows(ref)
+        at_pick = ref[0, tok[m]]
+        tol = 1e-2 + 1e-2 * abs(ref_max[0])
+        assert ref_max[0] - at_pick <= 2 * tol, f"{name} row {m}"
+        assert abs(val[m] - at_pick) <= 1e-2 + 1e-2 * abs(at_pick), f"{name} row {m}"
+
+
+def test_parallel_lmhead_layer_fold_argmax():
+    V, D, tp, m = 1000, 64, 4, 9
+    X, full = _int_inputs(390, m, V, D, "bf16")
+    full_d = to_dev(full)
+    best = torch.empty(m, dtype=torch.int64, device=dev())
+    vpe.vpe_argmax_init(best)
+    for r in reversed(range(tp)):
+        head = vpe.ParallelLMHead(V, D, tp_size=tp, tp_rank=r, device=dev())
+        head.weight_loader(head.weight, full_d)
+        head.fold_argmax(to_dev(X), best)
+    val, tok = vpe.vpe_argmax_decode(best)
+    ref_max, ref_idx = oracle.argmax_rows(oracle.lmhead_f64(X, full))
+    assert np.array_equal(to_host(tok), ref_idx)
+    assert np.array_equal(to_host(val).astype(np.float64), ref_max)

@@ -321,3 +321,30 @@ def test_lmhead_rejects_offset_past_row():
     W = np.zeros((3, 4), np.float32)
     with pytest.raises(oracle.OracleError):
         oracle.lmhead_f64(X, W, out=np.zeros((2, 4)), col_offset=2)
+
+
+# ---------------------------------------------------------------------------
+# greedy pick over logits
+# ---------------------------------------------------------------------------
+def test_argmax_rows_matches_numpy_first_maximum():
+    rng = np.random.default_rng(31)
+    z = rng.integers(-5, 6, size=(40, 57)).astype(np.float64)  # many exact ties
+    mx, idx = oracle.argmax_rows(z)
+    assert np.array_equal(idx, np.argmax(z, axis=1))            # numpy: first maximum
+    assert np.array_equal(mx, z.max(axis=1))
+
+
+def test_argmax_of_concatenated_shards_is_global_argmax():
+    V, D, M, tp = 96, 16, 9, 3
+    W = wl.table_rows(32, V, D, "f32", 0, V, std=1.0)
+    X = wl.hidden_states(33, M, D, "f32")
+    full = oracle.lmhead_f64(X, W)
+    cat = np.zeros((M, V))
+    for r in range(tp):
+        s, e = oracle.shard_range(V, tp, r)
+        oracle.lmhead_f64(X, W[s:e], out=cat, col_offset=s)
+    assert np.array_equal(oracle.argmax_rows(cat)[1], oracle.argmax_rows(full)[1])
+    # per-shard maxima combined by value (ties to the lower id) give the same pick
+    best = [max((oracle.argmax_rows(cat[:, s:e])[0][m], -(oracle.argmax_rows(cat[:, s:e])[1][m] + s))
+                for s, e in (oracle.shard_range(V, tp, r) for r in range(tp))) for m in range(M)]
+    assert [-b[1] for b in best] == list(oracle.argmax_rows(full)[1])

@@ -26,7 +26,9 @@ VPE_I32, VPE_I64 = 0, 1
 VPE_MAX_PARTS = 64
 
 EXPORTED_SYMBOLS = ("vpe_shard_range", "vpe_embed", "vpe_sum_partials",
-                    "vpe_last_token_select", "vpe_lmhead", "vpe_status_string")
+                    "vpe_last_token_select", "vpe_lmhead", "vpe_lmhead_prefill",
+                    "vpe_argmax_init", "vpe_lmhead_argmax", "vpe_argmax_decode",
+                    "vpe_status_string")
 
 
 class VpeError(RuntimeError):
@@ -56,6 +58,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.vpe_sum_partials.argtypes = [ctypes.POINTER(vp), i32, i64, ci, vp, vp]
     lib.vpe_last_token_select.argtypes = [vp, i64, i64, ci, vp, i64, vp, vp]
     lib.vpe_lmhead.argtypes = [vp, i64, i64, vp, i64, ci, vp, i64, i64, vp]
+    lib.vpe_lmhead_prefill.argtypes = [vp, i64, i64, vp, i64, vp, i64, ci, vp, i64, i64, vp]
+    lib.vpe_argmax_init.argtypes = [vp, i64, vp]
+    lib.vpe_lmhead_argmax.argtypes = [vp, i64, i64, vp, i64, ci, i64, vp, vp]
+    lib.vpe_argmax_decode.argtypes = [vp, i64, vp, vp, vp]
     for name in EXPORTED_SYMBOLS[:-1]:
         getattr(lib, name).restype = ci
     lib.vpe_status_string.argtypes = [ci]
@@ -221,9 +227,86 @@ def vpe_lmhead(x, weight, logits=None, col_offset: int = 0):
     return logits
 
 
+def vpe_lmhead_prefill(hidden, cu_seqlens, weight, logits=None, col_offset: int = 0):
+    """Logits of the last position of every packed sequence, select folded in.
+
+    hidden [T, D], cu_seqlens int32 [S+1], weight [R, D] -> logits [S, ld]
+    (columns [col_offset, col_offset + R) written).
+    """
+    torch = _torch()
+    _need_device("hidden", hidden)
+    _need_device("cu_seqlens", cu_seqlens)
+    _need_device("weight", weight)
+    if hidden.dim() != 2 or weight.dim() != 2 or hidden.shape[1] != weight.shape[1]:
+        raise ValueError("hidden must be [n_tokens, dim] and weight [shard_rows, dim]")
+    if hidden.dtype != weight.dtype:
+        raise TypeError("hidden and weight must share a dtype")
+    if cu_seqlens.dtype != torch.int32 or cu_seqlens.dim() != 1 or cu_seqlens.numel() < 1:
+        raise ValueError("cu_seqlens must be a 1-D int32 tensor with at least one entry")
+    t, d = hidden.shape
+    s = cu_seqlens.numel() - 1
+    rows = weight.shape[0]
+    if logits is None:
+        logits = torch.empty((s, col_offset + rows), dtype=hidden.dtype, device=hidden.device)
+    _need_device("logits", logits)
+    if logits.dim() != 2 or logits.shape[0] != s or logits.dtype != hidden.dtype:
+        raise ValueError("logits must be [n_seqs, ld] of hidden's dtype")
+    _same_device(hidden, cu_seqlens, weight, logits)
+    _check("vpe_lmhead_prefill", load_library().vpe_lmhead_prefill(
+        hidden.data_ptr(), t, d, cu_seqlens.data_ptr(), s, weight.data_ptr(), rows,
+        _dtype_code(hidden), logits.data_ptr(), logits.shape[1], int(col_offset),
+        _stream_handle(hidden.device)))
+    return logits
+
+
+def vpe_argmax_init(best):
+    """Reset the [m] uint64 (int64 tensor) greedy-pick keys to 0."""
+    torch = _torch()
+    _need_device("best", best)
+    if best.dtype != torch.int64 or best.dim() != 1:
+        raise ValueError("best must be a 1-D int64 tensor (uint64 keys)")
+    _check("vpe_argmax_init", load_library().vpe_argmax_init(
+        best.data_ptr(), best.numel(), _stream_handle(best.device)))
+    return best
+
+
+def vpe_lmhead_argmax(x, weight, vocab_start: int, best):
+    """Fold this shard's greedy pick (largest logit, id = vocab_start + row) into best."""
+    torch = _torch()
+    _need_device("x", x)
+    _need_device("weight", weight)
+    _need_device("best", best)
+    if x.dim() != 2 or weight.dim() != 2 or x.shape[1] != weight.shape[1]:
+        raise ValueError("x must be [m, dim] and weight [shard_rows, dim]")
+    if x.dtype != weight.dtype:
+        raise TypeError("x and weight must share a dtype")
+    if best.dtype != torch.int64 or best.numel() != x.shape[0]:
+        raise ValueError("best must be an int64 tensor with one key per row of x")
+    _same_device(x, weight, best)
+    _check("vpe_lmhead_argmax", load_library().vpe_lmhead_argmax(
+        x.data_ptr(), x.shape[0], x.shape[1], weight.data_ptr(), weight.shape[0],
+        _dtype_code(x), int(vocab_start), best.data_ptr(), _stream_handle(x.device)))
+    return best
+
+
+def vpe_argmax_decode(best):
+    """(max logit float32 [m], token id int64 [m]) from the keys."""
+    torch = _torch()
+    _need_device("best", best)
+    if best.dtype != torch.int64 or best.dim() != 1:
+        raise ValueError("best must be a 1-D int64 tensor (uint64 keys)")
+    value = torch.empty(best.shape, dtype=torch.float32, device=best.device)
+    token = torch.empty(best.shape, dtype=torch.int64, device=best.device)
+    _check("vpe_argmax_decode", load_library().vpe_argmax_decode(
+        best.data_ptr(), best.numel(), value.data_ptr(), token.data_ptr(),
+        _stream_handle(best.device)))
+    return value, token
+
+
 from .layers import ParallelLMHead, VocabParallelEmbedding  # noqa: E402
 
 __all__ = [
     "vpe_shard_range", "vpe_embed", "vpe_sum_partials", "vpe_last_token_select", "vpe_lmhead",
+    "vpe_lmhead_prefill", "vpe_argmax_init", "vpe_lmhead_argmax", "vpe_argmax_decode",
     "VocabParallelEmbedding", "ParallelLMHead", "VpeError", "load_library", "LIB_PATH",
 ]

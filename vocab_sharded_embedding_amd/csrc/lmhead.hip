@@ -42,6 +42,28 @@ __device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
 }
 
 // ---------------------------------------------------------------------------
+// Greedy-pick keys.  A logit v of vocabulary id t becomes the 64-bit key
+//   (order(v) << 32) | (0xFFFFFFFF - t)
+// where order() maps binary32 bits to an unsigned integer with the same
+// order as the values.  The largest key is the largest logit, and among
+// equal logits the smallest id (the first maximum, as an argmax over the
+// concatenated row picks).  Shards fold their candidates into one key per row
+// with an atomic max, so the combine across shards needs no extra step.
+// ---------------------------------------------------------------------------
+struct ArgmaxOut {
+  uint64_t *best;   // [M] keys, or nullptr: write logits instead
+  int64_t id_base;  // vocabulary id of the shard's first row (vocab_start)
+};
+
+__device__ __forceinline__ uint64_t pick_key(float v, int64_t id) {
+  const uint32_t u = __float_as_uint(v);
+  const uint32_t ord = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  return (static_cast<uint64_t>(ord) << 32) | (0xFFFFFFFFu - static_cast<uint32_t>(id));
+}
+
+__device__ __forceinline__ uint64_t umax64(uint64_t a, uint64_t b) { return a > b ? a : b; }
+
+// ---------------------------------------------------------------------------
 // LDS tile layout: a row holds BK bf16 = P = BK/8 pieces of 16 bytes.  The LDS
 // serves a 16-byte read in passes of 8 lanes over 32 four-byte banks (128
 // bytes), and the 8 lanes of a pass read the same piece of 8 consecutive
@@ -121,11 +143,18 @@ constexpr int vmcnt_imm(int n) { return (n & 0xF) | ((n >> 4) << 14) | (0x7 << 4
 // global loads of a later step; run the MFMAs.  One barrier per step, and
 // the LDS writes and global loads overlap the MFMAs.  In LDS, rows [0, BN)
 // hold the W slice and rows [BN, BN+BM) the X slice of a step.
-template <class C, bool VEC>
+//
+// GX (prefill): the M rows of X are not stored contiguously; row i is the
+// last position of packed sequence i, hidden[cu[i+1] - 1] with hidden
+// [n_tokens, K] (so the last-position select is folded into the staging).
+// ARGMAX: instead of storing logits, fold each row's largest logit (as
+// rounded to bf16) and its vocabulary id into pick.best[row].
+template <class C, bool VEC, bool GX, bool ARGMAX>
 __global__ __launch_bounds__(C::NT) void lmhead_bf16_mfma(
     const uint16_t *__restrict__ X, int64_t M, int64_t K, const uint16_t *__restrict__ W,
     int64_t N, uint16_t *__restrict__ out, int64_t ld, int64_t col_off, int tiles_n,
-    int tiles_m, int group_n) {
+    int tiles_m, int group_n, const int32_t *__restrict__ cu, int64_t n_tokens,
+    ArgmaxOut pick) {
   constexpr int BN = C::BN, BM = C::BM, WN = C::WN, WM = C::WM, BK = C::BK, PF = C::PF;
   constexpr int SWZ = C::SWZ, RS = C::RS, NT = C::NT, PIPE = C::PIPE;
   constexpr int TN = BN / WN, TM = BM / WM;
@@ -167,8 +196,20 @@ __global__ __launch_bounds__(C::NT) void lmhead_bf16_mfma(
   const __amdgpu_buffer_rsrc_t w_rsrc = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint16_t *>(W + n0 * K), 0, static_cast<int>(w_rows * K * 2), kBufferFlags);
   const __amdgpu_buffer_rsrc_t x_rsrc = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<uint16_t *>(X + m0 * K), 0, static_cast<int>(x_rows * K * 2), kBufferFlags);
+      const_cast<uint16_t *>(GX ? X : X + m0 * K), 0,
+      static_cast<int>((GX ? n_tokens : x_rows) * K * 2), kBufferFlags);
   const int row_bytes = static_cast<int>(K * 2);
+  // Element offset of X-tile row r from the X descriptor's base, or -1 when
+  // the row does not exist (past M, or a sequence end outside the tokens).
+  auto x_row_off = [&](int r) -> int64_t {
+    if (r >= x_rows) return -1;
+    if constexpr (GX) {
+      const int64_t t = static_cast<int64_t>(cu[m0 + r + 1]) - 1;
+      return (static_cast<uint64_t>(t) < static_cast<uint64_t>(n_tokens)) ? t * K : -1;
+    } else {
+      return static_cast<int64_t>(r) * K;
+    }
+  };
   const int voff0 = srow * row_bytes + spiece * 16;
   const int row_stride_bytes = kRowsPerPass * row_bytes;
 
@@ -184,16 +225,23 @@ __global__ __launch_bounds__(C::NT) void lmhead_bf16_mfma(
       const bool in_w = (BN % kRowsPerPass == 0) ? (p * kRowsPerPass < BN) : (row < BN);
       const int r = in_w ? row : row - BN;  // row inside W's or X's part of the tile
       if (VEC) {
-        const int voff = (BN % kRowsPerPass == 0)
-                             ? voff0 + (in_w ? p : p - BN / kRowsPerPass) * row_stride_bytes
-                             : r * row_bytes + spiece * 16;
+        int voff;
+        if (GX && !in_w) {
+          const int64_t xo = (row < kRows) ? x_row_off(r) : -1;
+          voff = xo >= 0 ? static_cast<int>(xo * 2) + spiece * 16 : 0x7FFF0000;
+        } else {
+          voff = (BN % kRowsPerPass == 0)
+                     ? voff0 + (in_w ? p : p - BN / kRowsPerPass) * row_stride_bytes
+                     : r * row_bytes + spiece * 16;
+        }
         dst[p] = __builtin_amdgcn_raw_buffer_load_b128(in_w ? w_rsrc : x_rsrc, voff,
                                                        static_cast<int>(k0 * 2), 0);
       } else {
         const int64_t gk = k0 + spiece * 8;
         u32x4 v = u32x4(0);
-        if (row < kRows && r < (in_w ? w_rows : x_rows)) {
-          const uint16_t *q = (in_w ? W + (n0 + r) * K : X + (m0 + r) * K) + gk;
+        const int64_t xo = (!in_w && row < kRows) ? x_row_off(r) : -1;
+        if (row < kRows && (in_w ? r < w_rows : xo >= 0)) {
+          const uint16_t *q = (in_w ? W + (n0 + r) * K : (GX ? X : X + m0 * K) + xo) + gk;
           uint16_t e[8];
 #pragma unroll
           for (int i = 0; i < 8; ++i) e[i] = (gk + i < K) ? q[i] : uint16_t(0);
@@ -267,7 +315,49 @@ __global__ __launch_bounds__(C::NT) void lmhead_bf16_mfma(
     // One step into stage buffer `buf`: lane l of wave w fills LDS slot l % P
     // of tile row p * kRowsPerPass + w * (64 / P) + l / P, which holds piece
     // slot ^ f(row) of that row (the swizzle is applied on the global side).
-    auto dma_step = [&](int step, int buf) {
+    // byte offset of this lane's row in each pass from its descriptor's base,
+    // or -1 for rows past the matrices (fixed for the whole tile)
+    int row_off[kPPT];
+    // gathered X: the sequence ends, loaded before any tile data (see below)
+    int32_t cu_end[kPPT];
+#pragma unroll
+    for (int p = 0; p < kPPT; ++p) {
+      const int row0 = p * kRowsPerPass + wave_u * kRowsPerWaveLoad;
+      const int row = row0 + lrow;
+      const bool in_w = (BN % kRowsPerPass == 0) ? (p * kRowsPerPass < BN) : (row0 < BN);
+      cu_end[p] = 0;
+      if (in_w) {
+        row_off[p] = row < w_rows_i ? row * row_bytes : -1;
+      } else if constexpr (GX) {
+        const int r = row - BN;
+        const bool exists = row < kRows && r < x_rows_i;
+        row_off[p] = -1;
+        if (exists) cu_end[p] = cu[m0 + r + 1];
+      } else {
+        const int64_t xo = (row < kRows) ? x_row_off(row - BN) : -1;
+        row_off[p] = xo >= 0 ? static_cast<int>(xo * 2) : -1;
+      }
+    }
+    // X row offsets of a gathered X, from the sequence ends; the first use of
+    // the loaded ends comes after stage 0's W loads have been issued, so their
+    // latency overlaps (vmcnt is in order: the ends were issued first)
+    auto gather_offsets = [&]() {
+#pragma unroll
+      for (int p = 0; p < kPPT; ++p) {
+        const int row0 = p * kRowsPerPass + wave_u * kRowsPerWaveLoad;
+        const int row = row0 + lrow;
+        const bool in_w = (BN % kRowsPerPass == 0) ? (p * kRowsPerPass < BN) : (row0 < BN);
+        if (in_w) continue;
+        asm volatile("" : "+v"(cu_end[p]));
+        const int r = row - BN;
+        const int64_t t = static_cast<int64_t>(cu_end[p]) - 1;
+        const bool ok = row < kRows && r < x_rows_i &&
+                        static_cast<uint64_t>(t) < static_cast<uint64_t>(n_tokens);
+        row_off[p] = ok ? static_cast<int>(t * K * 2) : -1;
+      }
+    };
+    // part: 0 = the whole step, 1 = only passes that start inside W, 2 = the rest
+    auto dma_step = [&](int step, int buf, int part = 0) {
       const int k0 = (step < nk_i ? step : nk_i - 1) * BK;
       uint16_t *base = lds[buf];
 #pragma unroll
@@ -278,16 +368,24 @@ __global__ __launch_bounds__(C::NT) void lmhead_bf16_mfma(
         bool in_w;
         if constexpr (BN % kRowsPerPass == 0) in_w = p * kRowsPerPass < BN;
         else in_w = row0 < BN;
-        const int r = in_w ? row : row - BN;
-        const bool ok = r < (in_w ? w_rows_i : x_rows_i) && k0 + piece * 8 < k_i;
-        const int voff = ok ? r * row_bytes + piece * 16 : kBig;
+        if (part == 1 && !in_w) continue;
+        if (part == 2 && in_w) continue;
+        const bool ok = row_off[p] >= 0 && k0 + piece * 8 < k_i;
+        const int voff = ok ? row_off[p] + piece * 16 : kBig;
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
             in_w ? w_rsrc : x_rsrc, (__attribute__((address_space(3))) void *)(base + row0 * BK),
             16, voff, k0 * 2, 0, 0);
       }
     };
+    // Stage 0's W loads go out before the first use of the X row offsets, so
+    // that a gathered X (whose offsets wait on loads of cu) costs no latency.
+    // Stage 0 is still wholly issued before stages 1.., which is all the
+    // vmcnt count below relies on.
+    dma_step(0, 0, 1);
+    if constexpr (GX) gather_offsets();
+    dma_step(0, 0, 2);
 #pragma unroll
-    for (int st = 0; st < NS - 1; ++st) dma_step(st, st);
+    for (int st = 1; st < NS - 1; ++st) dma_step(st, st);
     int rd = 0, wr = NS - 1;  // stage buffers read and refilled by the current step
     for (int kt = 0; kt < nk_i; ++kt) {
       // this wave's loads of step kt have landed once at most the later
@@ -396,6 +494,29 @@ __global__ __launch_bounds__(C::NT) void lmhead_bf16_mfma(
   }
   }  // PIPE == 0
 
+  if constexpr (ARGMAX) {
+    // the 4 lanes l, l^16, l^32, l^48 hold the same row m (16 columns each)
+    const int64_t nbase = n0 + wn * TN + 4 * frag_grp;
+#pragma unroll
+    for (int j = 0; j < FM; ++j) {
+      const int64_t m = m0 + wm * TM + j * 16 + frag_row;
+      uint64_t key = 0;
+#pragma unroll
+      for (int i = 0; i < FN; ++i)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int64_t n = nbase + i * 16 + r;
+          const float v = __uint_as_float(f32_to_bf16_bits(acc[i][j][r]) << 16);
+          if (n < N) key = umax64(key, pick_key(v, pick.id_base + n));
+        }
+      key = umax64(key, __shfl_xor(key, 16));
+      key = umax64(key, __shfl_xor(key, 32));
+      if (frag_grp == 0 && m < M) atomicMax(reinterpret_cast<unsigned long long *>(pick.best + m),
+                                            static_cast<unsigned long long>(key));
+    }
+    return;
+  }
+
   // acc[i][j][r] = Z^T[n = 4*(lane/16) + r][m = lane%16] of fragment (i, j).
   // 8-byte stores need every row start at a multiple of 4 elements from an
   // 8-byte-aligned base (column offsets inside a tile are multiples of 4).
@@ -440,10 +561,16 @@ __global__ __launch_bounds__(C::NT) void lmhead_bf16_mfma(
 // ---------------------------------------------------------------------------
 // fp32: 64 x 64 output tile per workgroup, 4 x 4 outputs per thread.
 // ---------------------------------------------------------------------------
+// With cu != nullptr, row i of X is hidden[cu[i+1] - 1] of X = hidden [n_tokens, K]
+// (zeros when that index is outside [0, n_tokens)).
+// With pick.best != nullptr each row's largest logit and its id are folded
+// into pick.best[row] instead of storing the logits.
 __global__ __launch_bounds__(kBlock) void lmhead_f32_tiled(const float *__restrict__ X, int64_t M,
                                                           int64_t K, const float *__restrict__ W,
                                                           int64_t N, float *__restrict__ out,
-                                                          int64_t ld, int64_t col_off) {
+                                                          int64_t ld, int64_t col_off,
+                                                          const int32_t *__restrict__ cu,
+                                                          int64_t n_tokens, ArgmaxOut pick) {
   constexpr int T = 64, TK = 16;
   __shared__ float sX[TK][T + 1];
   __shared__ float sW[TK][T + 1];
@@ -455,7 +582,13 @@ __global__ __launch_bounds__(kBlock) void lmhead_f32_tiled(const float *__restri
     for (int e = threadIdx.x; e < T * TK; e += kBlock) {
       const int r = e / TK, kk = e % TK;
       const int64_t k = k0 + kk;
-      sX[kk][r] = (m0 + r < M && k < K) ? X[(m0 + r) * K + k] : 0.f;
+      int64_t xr = m0 + r;
+      bool xok = xr < M && k < K;
+      if (cu != nullptr && xok) {
+        xr = static_cast<int64_t>(cu[m0 + r + 1]) - 1;
+        xok = static_cast<uint64_t>(xr) < static_cast<uint64_t>(n_tokens);
+      }
+      sX[kk][r] = xok ? X[xr * K + k] : 0.f;
       sW[kk][r] = (n0 + r < N && k < K) ? W[(n0 + r) * K + k] : 0.f;
     }
     __syncthreads();
@@ -473,6 +606,24 @@ __global__ __launch_bounds__(kBlock) void lmhead_f32_tiled(const float *__restri
     }
     __syncthreads();
   }
+  if (pick.best != nullptr) {
+    // the 16 threads with the same ty (consecutive lanes) share rows ty*4 + i
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int64_t m = m0 + ty * 4 + i;
+      uint64_t key = 0;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int64_t n = n0 + tx * 4 + j;
+        if (n < N) key = umax64(key, pick_key(acc[i][j], pick.id_base + n));
+      }
+#pragma unroll
+      for (int d = 1; d < 16; d <<= 1) key = umax64(key, __shfl_xor(key, d));
+      if (tx == 0 && m < M) atomicMax(reinterpret_cast<unsigned long long *>(pick.best + m),
+                                      static_cast<unsigned long long>(key));
+    }
+    return;
+  }
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int64_t m = m0 + ty * 4 + i;
@@ -485,35 +636,73 @@ __global__ __launch_bounds__(kBlock) void lmhead_f32_tiled(const float *__restri
   }
 }
 
+__global__ __launch_bounds__(kBlock) void argmax_init_kernel(uint64_t *__restrict__ best, int64_t m) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * kBlock + threadIdx.x;
+  if (i < m) best[i] = 0;
+}
+
+// key -> (logit, id): the inverse of pick_key
+__global__ __launch_bounds__(kBlock) void argmax_decode_kernel(const uint64_t *__restrict__ best,
+                                                              int64_t m, float *__restrict__ value,
+                                                              int64_t *__restrict__ id) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * kBlock + threadIdx.x;
+  if (i >= m) return;
+  const uint64_t key = best[i];
+  const uint32_t ord = static_cast<uint32_t>(key >> 32);
+  const uint32_t u = (ord & 0x80000000u) ? (ord & 0x7FFFFFFFu) : ~ord;
+  if (value != nullptr) value[i] = __uint_as_float(u);
+  if (id != nullptr) id[i] = static_cast<int64_t>(0xFFFFFFFFu - static_cast<uint32_t>(key));
+}
+
 template <class C>
 int launch_bf16_cfg(const uint16_t *x, int64_t m, int64_t k, const uint16_t *w, int64_t n,
-                    uint16_t *out, int64_t ld, int64_t col_off, hipStream_t st, int group_n = 1) {
+                    uint16_t *out, int64_t ld, int64_t col_off, hipStream_t st, int group_n = 1,
+                    const int32_t *cu = nullptr, int64_t n_tokens = 0,
+                    ArgmaxOut pick = ArgmaxOut{nullptr, 0}) {
   const int64_t tn64 = (n + C::BN - 1) / C::BN, tm64 = (m + C::BM - 1) / C::BM;
   if (tn64 * tm64 > INT32_MAX) return static_cast<int>(hipErrorInvalidValue);
   const int tiles_n = static_cast<int>(tn64);
   const int tiles_m = static_cast<int>(tm64);
   const dim3 grid(static_cast<unsigned>(tiles_n) * static_cast<unsigned>(tiles_m));
-  const bool vec = (k % 8 == 0) && ((reinterpret_cast<uint64_t>(x) | reinterpret_cast<uint64_t>(w)) & 15) == 0;
-  if (vec)
-    hipLaunchKernelGGL((lmhead_bf16_mfma<C, true>), grid, dim3(C::NT), 0, st, x, m, k, w, n, out,
-                       ld, col_off, tiles_n, tiles_m, group_n);
-  else
-    hipLaunchKernelGGL((lmhead_bf16_mfma<C, false>), grid, dim3(C::NT), 0, st, x, m, k, w, n,
-                       out, ld, col_off, tiles_n, tiles_m, group_n);
+  const bool gx = cu != nullptr;
+  // 16-byte buffer loads need 16-byte rows and bases, and every byte offset of
+  // a gathered X row must fit the descriptor's 32-bit range
+  const bool vec = (k % 8 == 0) &&
+                   ((reinterpret_cast<uint64_t>(x) | reinterpret_cast<uint64_t>(w)) & 15) == 0 &&
+                   (!gx || n_tokens * k * 2 < (int64_t(1) << 31));
+#define VPE_LAUNCH(V, G)                                                                     \
+  do {                                                                                       \
+    if (pick.best)                                                                           \
+      hipLaunchKernelGGL((lmhead_bf16_mfma<C, V, G, true>), grid, dim3(C::NT), 0, st, x, m, k, w, \
+                         n, out, ld, col_off, tiles_n, tiles_m, group_n, cu, n_tokens, pick);  \
+    else                                                                                     \
+      hipLaunchKernelGGL((lmhead_bf16_mfma<C, V, G, false>), grid, dim3(C::NT), 0, st, x, m, k,  \
+                         w, n, out, ld, col_off, tiles_n, tiles_m, group_n, cu, n_tokens, pick); \
+  } while (0)
+  if (gx) {
+    if (vec) VPE_LAUNCH(true, true);
+    else VPE_LAUNCH(false, true);
+  } else {
+    if (vec) VPE_LAUNCH(true, false);
+    else VPE_LAUNCH(false, false);
+  }
+#undef VPE_LAUNCH
   return 0;
 }
 
 }  // namespace
 
 int launch_lmhead(const void *x, int64_t m, int64_t k, const void *w, int64_t n, int dtype,
-                  void *logits, int64_t ld, int64_t col_offset, void *stream) {
+                  void *logits, int64_t ld, int64_t col_offset, void *stream,
+                  const int32_t *cu, int64_t n_tokens, uint64_t *best, int64_t id_base) {
+  const ArgmaxOut pick{best, id_base};
   hipStream_t st = static_cast<hipStream_t>(stream);
   (void)hipGetLastError();  // clear a stale error so the status below is this launch's
   if (dtype == 0) {
     const dim3 grid(static_cast<unsigned>((n + 63) / 64), static_cast<unsigned>((m + 63) / 64));
     hipLaunchKernelGGL(lmhead_f32_tiled, grid, dim3(kBlock), 0, st, static_cast<const float *>(x),
                        m, k, static_cast<const float *>(w), n, static_cast<float *>(logits), ld,
-                       col_offset);
+                       col_offset, cu, n_tokens, pick);
     return static_cast<int>(hipGetLastError());
   }
   const uint16_t *xb = static_cast<const uint16_t *>(x);
@@ -523,24 +712,43 @@ int launch_lmhead(const void *x, int64_t m, int64_t k, const void *w, int64_t n,
   //  - M <= 64 (decode-size batches): the LM head streams W once and is
   //    bound by HBM; narrow tiles of 128 vocabulary rows keep ~1200 tiles
   //    in flight and four LDS stages keep W loads well ahead of the MFMAs;
-  //  - M <= 256: 160 vocabulary rows per tile (475 tiles for a 75968-row
-  //    shard, under two rounds over 256 CUs), two LDS stages;
-  //  - larger M is a dense contraction: 256 x 256 tiles over 8 waves, two
-  //    LDS stages, tiles grouped 4 W blocks wide for L2 reuse.
+  //  - M > 128: 320 vocabulary rows x 256 hidden rows over 8 waves (a wave
+  //    owns 160 x 64), two LDS stages.  A 75968-row shard is 238 W tiles:
+  //    one round over 256 CUs at M = 256, X re-read once per W tile, and
+  //    0.35 KB of LDS fragment reads per MFMA.
   int rc;
   if (m <= 16)
-    rc = launch_bf16_cfg<Cfg<128, 16, 4, 1, 64, 1, 0, 0, 2, 4>>(xb, m, k, wb, n, ob, ld, col_offset, st);
+    rc = launch_bf16_cfg<Cfg<128, 16, 4, 1, 64, 1, 0, 0, 2, 4>>(xb, m, k, wb, n, ob, ld, col_offset, st, 1, cu, n_tokens, pick);
   else if (m <= 32)
-    rc = launch_bf16_cfg<Cfg<128, 32, 4, 1, 64, 1, 0, 0, 2, 4>>(xb, m, k, wb, n, ob, ld, col_offset, st);
+    rc = launch_bf16_cfg<Cfg<128, 32, 4, 1, 64, 1, 0, 0, 2, 4>>(xb, m, k, wb, n, ob, ld, col_offset, st, 1, cu, n_tokens, pick);
   else if (m <= 64)
-    rc = launch_bf16_cfg<Cfg<128, 64, 4, 1, 64, 1, 0, 0, 2, 4>>(xb, m, k, wb, n, ob, ld, col_offset, st);
+    rc = launch_bf16_cfg<Cfg<128, 64, 4, 1, 64, 1, 0, 0, 2, 4>>(xb, m, k, wb, n, ob, ld, col_offset, st, 1, cu, n_tokens, pick);
   else if (m <= 128)
-    rc = launch_bf16_cfg<Cfg<256, 128, 4, 2, 64, 1, 0, 0, 2, 3>>(xb, m, k, wb, n, ob, ld, col_offset, st, 4);
-  else if (m <= 256)
-    rc = launch_bf16_cfg<Cfg<160, 256, 2, 4, 64, 1, 0, 0, 2, 2>>(xb, m, k, wb, n, ob, ld, col_offset, st);
+    rc = launch_bf16_cfg<Cfg<256, 128, 4, 2, 64, 1, 0, 0, 2, 3>>(xb, m, k, wb, n, ob, ld, col_offset, st, 4, cu, n_tokens, pick);
   else
-    rc = launch_bf16_cfg<Cfg<256, 256, 2, 4, 64, 1, 0, 0, 2, 2>>(xb, m, k, wb, n, ob, ld, col_offset, st, 4);
+    rc = launch_bf16_cfg<Cfg<320, 256, 2, 4, 64, 1, 0, 0, 2, 2>>(xb, m, k, wb, n, ob, ld, col_offset, st, 1, cu, n_tokens, pick);
   if (rc != 0) return rc;
+  return static_cast<int>(hipGetLastError());
+}
+
+}  // namespace vpe
+
+namespace vpe {
+
+int launch_argmax_init(uint64_t *best, int64_t m, void *stream) {
+  (void)hipGetLastError();
+  const dim3 grid(static_cast<unsigned>((m + kBlock - 1) / kBlock));
+  hipLaunchKernelGGL(argmax_init_kernel, grid, dim3(kBlock), 0, static_cast<hipStream_t>(stream),
+                     best, m);
+  return static_cast<int>(hipGetLastError());
+}
+
+int launch_argmax_decode(const uint64_t *best, int64_t m, float *value, int64_t *id,
+                         void *stream) {
+  (void)hipGetLastError();
+  const dim3 grid(static_cast<unsigned>((m + kBlock - 1) / kBlock));
+  hipLaunchKernelGGL(argmax_decode_kernel, grid, dim3(kBlock), 0,
+                     static_cast<hipStream_t>(stream), best, m, value, id);
   return static_cast<int>(hipGetLastError());
 }
 

@@ -27,8 +27,22 @@ int launch_sum_partials(const void *const *parts, int n_parts, int64_t n_elems, 
                         void *out, void *stream);
 
 // logits[i*ld + col_offset + j] = sum_k x[i,k] w[j,k].  dtype: 0 = f32, 1 = bf16.
+// With cu != nullptr, x is hidden [n_tokens, k] and row i of the product is
+// hidden[cu[i+1] - 1] (prefill: last position of packed sequence i).
+// With best != nullptr, no logits are stored: each row's largest logit (as
+// rounded to the dtype) and its id (id_base + column) are folded into the
+// 64-bit key best[i] by atomic max.
 int launch_lmhead(const void *x, int64_t m, int64_t k, const void *w, int64_t n, int dtype,
-                  void *logits, int64_t ld, int64_t col_offset, void *stream);
+                  void *logits, int64_t ld, int64_t col_offset, void *stream,
+                  const int32_t *cu = nullptr, int64_t n_tokens = 0, uint64_t *best = nullptr,
+                  int64_t id_base = 0);
+
+// best[i] = 0 for i < m.
+int launch_argmax_init(uint64_t *best, int64_t m, void *stream);
+
+// value[i], id[i] decoded from best[i] (either output may be null).
+int launch_argmax_decode(const uint64_t *best, int64_t m, float *value, int64_t *id,
+                         void *stream);
 
 }  // namespace vpe
 

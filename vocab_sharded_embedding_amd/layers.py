@@ -17,7 +17,8 @@ from typing import Optional, Sequence
 
 import torch
 
-from . import vpe_embed, vpe_last_token_select, vpe_lmhead, vpe_shard_range, vpe_sum_partials
+from . import (vpe_embed, vpe_lmhead, vpe_lmhead_argmax, vpe_lmhead_prefill, vpe_shard_range,
+               vpe_sum_partials)
 
 
 class VocabParallelEmbedding(torch.nn.Module):
@@ -67,11 +68,20 @@ class ParallelLMHead(VocabParallelEmbedding):
         is projected.  ``logits`` may be this rank's [M, V/tp] buffer or the
         full [M, V] buffer, in which case the shard lands at its vocab_start.
         """
-        x = hidden if cu_seqlens is None else vpe_last_token_select(hidden, cu_seqlens)
         if logits is None:
-            return vpe_lmhead(x, self.weight)
-        if logits.shape[1] == self.num_embeddings_per_partition:
-            return vpe_lmhead(x, self.weight, logits, col_offset=0)
-        if logits.shape[1] == self.num_embeddings:
-            return vpe_lmhead(x, self.weight, logits, col_offset=self.vocab_start_idx)
-        raise ValueError("logits must be [M, V/tp] (one shard) or [M, V] (all shards)")
+            col = 0
+        elif logits.shape[1] == self.num_embeddings_per_partition:
+            col = 0
+        elif logits.shape[1] == self.num_embeddings:
+            col = self.vocab_start_idx
+        else:
+            raise ValueError("logits must be [M, V/tp] (one shard) or [M, V] (all shards)")
+        if cu_seqlens is not None:
+            # the last-position select is folded into the LM-head kernel
+            return vpe_lmhead_prefill(hidden, cu_seqlens, self.weight, logits, col_offset=col)
+        return vpe_lmhead(hidden, self.weight, logits, col_offset=col)
+
+    def fold_argmax(self, hidden: torch.Tensor, best: torch.Tensor) -> torch.Tensor:
+        """Fold this rank's greedy pick for every row of ``hidden`` into ``best``
+        (keys reset by ``vpe_argmax_init``; read with ``vpe_argmax_decode``)."""
+        return vpe_lmhead_argmax(hidden, self.weight, self.vocab_start_idx, best)
