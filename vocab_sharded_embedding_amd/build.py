@@ -58,7 +58,10 @@ def build(verbose: bool = False) -> str:
         for f in [ex.submit(_run, j) for j in jobs]:
             f.result()
     tmp = LIB + ".tmp%d" % os.getpid()
-    _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp])
+    # --no-undefined: a kernel whose host launch stub was not emitted fails here,
+    # not at load time
+    _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-Wl,--no-undefined", *objs,
+          "-o", tmp])
     os.replace(tmp, LIB)
     if verbose:
         print(f"built {LIB}")

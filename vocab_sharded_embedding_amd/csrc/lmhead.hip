@@ -63,6 +63,10 @@ __device__ __forceinline__ uint64_t pick_key(float v, int64_t id) {
 
 __device__ __forceinline__ uint64_t umax64(uint64_t a, uint64_t b) { return a > b ? a : b; }
 
+// Makes v's value needed at this point of the program, so the load that
+// produces it is issued earlier and waited on here, not later.
+__device__ __forceinline__ void pin_vgpr(int32_t &v) { asm volatile("" : "+v"(v)); }
+
 // ---------------------------------------------------------------------------
 // LDS tile layout: a row holds BK bf16 = P = BK/8 pieces of 16 bytes.  The LDS
 // serves a 16-byte read in passes of 8 lanes over 32 four-byte banks (128
@@ -104,6 +108,80 @@ __device__ __forceinline__ void tile_of_block(int b, int tiles_n, int tiles_m, i
   const int gn = min(group_n, tiles_n - g * group_n);  // the last group may be narrower
   tm = in_g / gn;
   tn = g * group_n + (in_g - tm * gn);
+}
+
+// Offset past any descriptor's range: buffer loads at it return zeros.  Every
+// descriptor built here covers at most kBig bytes.
+constexpr int kBig = 0x7FFF0000;
+
+// Writes a wave's accumulators.  acc[i][j][r] = Z^T[n][m] for the vocabulary
+// row n = nb + 16 i + r and hidden row m = mb + 16 j, where nb and mb are the
+// lane's first column and row (nb is a multiple of 4 from a multiple-of-4
+// tile origin).  `full`: the workgroup tile lies wholly inside [0, N) x [0, M).
+// ARGMAX folds each row's largest logit (rounded to bf16) into pick.best.
+template <int FN, int FM, bool ARGMAX>
+__device__ __forceinline__ void write_tile(const f32x4 (&acc)[FN][FM], int64_t nb, int64_t mb,
+                                           bool full, int64_t M, int64_t N,
+                                           uint16_t *__restrict__ out, int64_t ld,
+                                           int64_t col_off, ArgmaxOut pick) {
+  if constexpr (ARGMAX) {
+    // the 4 lanes l, l^16, l^32, l^48 hold the same row m (16 columns each)
+#pragma unroll
+    for (int j = 0; j < FM; ++j) {
+      const int64_t m = mb + j * 16;
+      uint64_t key = 0;
+#pragma unroll
+      for (int i = 0; i < FN; ++i)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int64_t n = nb + i * 16 + r;
+          const float v = __uint_as_float(f32_to_bf16_bits(acc[i][j][r]) << 16);
+          if (n < N) key = umax64(key, pick_key(v, pick.id_base + n));
+        }
+      key = umax64(key, __shfl_xor(key, 16));
+      key = umax64(key, __shfl_xor(key, 32));
+      if ((threadIdx.x & 48) == 0 && m < M)
+        atomicMax(reinterpret_cast<unsigned long long *>(pick.best + m),
+                  static_cast<unsigned long long>(key));
+    }
+    return;
+  }
+  // 8-byte stores need every row start at a multiple of 4 elements from an
+  // 8-byte-aligned base (column offsets inside a tile are multiples of 4).
+  const bool pack_ok =
+      ((ld | col_off) & 3) == 0 && (reinterpret_cast<uintptr_t>(out) & 7) == 0;
+  if (pack_ok && full) {
+    // whole tile in range: no per-element checks
+#pragma unroll
+    for (int j = 0; j < FM; ++j) {
+      uint16_t *row = out + (mb + j * 16) * ld + col_off + nb;
+#pragma unroll
+      for (int i = 0; i < FN; ++i) {
+        const u32x2 v{f32_to_bf16_bits(acc[i][j][0]) | (f32_to_bf16_bits(acc[i][j][1]) << 16),
+                      f32_to_bf16_bits(acc[i][j][2]) | (f32_to_bf16_bits(acc[i][j][3]) << 16)};
+        *reinterpret_cast<u32x2 *>(row + i * 16) = v;
+      }
+    }
+    return;
+  }
+#pragma unroll
+  for (int j = 0; j < FM; ++j) {
+    const int64_t m = mb + j * 16;
+    if (m >= M) continue;
+#pragma unroll
+    for (int i = 0; i < FN; ++i) {
+      const int64_t n = nb + i * 16;
+      uint16_t *dst = out + m * ld + col_off + n;
+      if (pack_ok && n + 3 < N) {
+        const u32x2 v{f32_to_bf16_bits(acc[i][j][0]) | (f32_to_bf16_bits(acc[i][j][1]) << 16),
+                      f32_to_bf16_bits(acc[i][j][2]) | (f32_to_bf16_bits(acc[i][j][3]) << 16)};
+        *reinterpret_cast<u32x2 *>(dst) = v;
+      } else {
+        for (int r = 0; r < 4; ++r)
+          if (n + r < N) dst[r] = static_cast<uint16_t>(f32_to_bf16_bits(acc[i][j][r]));
+      }
+    }
+  }
 }
 
 // Tile configuration of the bf16 kernel.
@@ -228,7 +306,7 @@ __global__ __launch_bounds__(C::NT) void lmhead_bf16_mfma(
         int voff;
         if (GX && !in_w) {
           const int64_t xo = (row < kRows) ? x_row_off(r) : -1;
-          voff = xo >= 0 ? static_cast<int>(xo * 2) + spiece * 16 : 0x7FFF0000;
+          voff = xo >= 0 ? static_cast<int>(xo * 2) + spiece * 16 : kBig;
         } else {
           voff = (BN % kRowsPerPass == 0)
                      ? voff0 + (in_w ? p : p - BN / kRowsPerPass) * row_stride_bytes
@@ -308,7 +386,6 @@ __global__ __launch_bounds__(C::NT) void lmhead_bf16_mfma(
     static_assert((NS - 2) * kPPT <= 63, "outstanding loads must fit the vmcnt counter");
     const int wave_u = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6);
     const int lrow = lane / kPieces, lslot = lane % kPieces;
-    constexpr int kBig = 0x7FFF0000;  // offset past any descriptor's range: loads return 0
     const int nk_i = static_cast<int>(nk);
     const int k_i = static_cast<int>(K);
     const int w_rows_i = static_cast<int>(w_rows), x_rows_i = static_cast<int>(x_rows);
@@ -348,7 +425,7 @@ __global__ __launch_bounds__(C::NT) void lmhead_bf16_mfma(
         const int row = row0 + lrow;
         const bool in_w = (BN % kRowsPerPass == 0) ? (p * kRowsPerPass < BN) : (row0 < BN);
         if (in_w) continue;
-        asm volatile("" : "+v"(cu_end[p]));
+        pin_vgpr(cu_end[p]);
         const int r = row - BN;
         const int64_t t = static_cast<int64_t>(cu_end[p]) - 1;
         const bool ok = row < kRows && r < x_rows_i &&
@@ -494,68 +571,211 @@ __global__ __launch_bounds__(C::NT) void lmhead_bf16_mfma(
   }
   }  // PIPE == 0
 
-  if constexpr (ARGMAX) {
-    // the 4 lanes l, l^16, l^32, l^48 hold the same row m (16 columns each)
-    const int64_t nbase = n0 + wn * TN + 4 * frag_grp;
-#pragma unroll
-    for (int j = 0; j < FM; ++j) {
-      const int64_t m = m0 + wm * TM + j * 16 + frag_row;
-      uint64_t key = 0;
-#pragma unroll
-      for (int i = 0; i < FN; ++i)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int64_t n = nbase + i * 16 + r;
-          const float v = __uint_as_float(f32_to_bf16_bits(acc[i][j][r]) << 16);
-          if (n < N) key = umax64(key, pick_key(v, pick.id_base + n));
-        }
-      key = umax64(key, __shfl_xor(key, 16));
-      key = umax64(key, __shfl_xor(key, 32));
-      if (frag_grp == 0 && m < M) atomicMax(reinterpret_cast<unsigned long long *>(pick.best + m),
-                                            static_cast<unsigned long long>(key));
-    }
-    return;
-  }
+  // the clamped loads past the last step may still be landing in LDS
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+  write_tile<FN, FM, ARGMAX>(acc, n0 + wn * TN + 4 * frag_grp, m0 + wm * TM + frag_row,
+                             n0 + BN <= N && m0 + BM <= M, M, N, out, ld, col_off, pick);
+}
 
-  // acc[i][j][r] = Z^T[n = 4*(lane/16) + r][m = lane%16] of fragment (i, j).
-  // 8-byte stores need every row start at a multiple of 4 elements from an
-  // 8-byte-aligned base (column offsets inside a tile are multiples of 4).
-  const bool pack_ok =
-      ((ld | col_off) & 3) == 0 && (reinterpret_cast<uintptr_t>(out) & 7) == 0;
-  const int64_t nb = n0 + wn * TN + 4 * frag_grp;
-  const int64_t mb = m0 + wm * TM + frag_row;
-  if (pack_ok && n0 + BN <= N && m0 + BM <= M) {
-    // whole tile in range: no per-element checks
+// One step of W into an LDS stage: lane l of wave w fills, in pass p, LDS
+// slot l % 8 of tile row p * kRowsPerPass + 8 w + l / 8 with that row's piece
+// slot ^ f(row); w_off[p] is the row's byte offset (-1: no such row).
+// (The descriptor over [w, w + bytes) is built here from plain arguments.)
+template <int kPPT, int kRowsPerPass, int BK>
+__device__ __forceinline__ void xreg_dma_w(const uint16_t *w, int bytes, uint16_t *base,
+                                           const int (&w_off)[kPPT], int k0, int k_i, int wave,
+                                           int lrow, int lslot) {
+  const __amdgpu_buffer_rsrc_t rsrc =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t *>(w), 0, bytes, kBufferFlags);
+#pragma unroll
+  for (int p = 0; p < kPPT; ++p) {
+    const int row0 = p * kRowsPerPass + wave * 8;  // wave-uniform
+    const int piece = lslot ^ lds_swizzle<BK, 0>(row0 + lrow);
+    const bool ok = w_off[p] >= 0 && k0 + piece * 8 < k_i;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        rsrc, (__attribute__((address_space(3))) void *)(base + row0 * BK), 16,
+        ok ? w_off[p] + piece * 16 : kBig, k0 * 2, 0, 0);
+  }
+}
+
+// One step of X fragments into registers, in the MFMA operand layout: lane l
+// reads the 8 bf16 at k = k0 + 32 ks + 8 (l / 16) of its row j (byte offset
+// x_off[j] from x, -1: no such row); pieces past K read as zeros.
+template <int KS, int FM>
+__device__ __forceinline__ void xreg_load_x(const uint16_t *x, int bytes, bf16x8 (&dst)[KS][FM],
+                                            const int (&x_off)[FM], int k0, int k_i,
+                                            int frag_grp) {
+  const __amdgpu_buffer_rsrc_t rsrc =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t *>(x), 0, bytes, kBufferFlags);
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
     for (int j = 0; j < FM; ++j) {
-      uint16_t *row = out + (mb + j * 16) * ld + col_off + nb;
-#pragma unroll
-      for (int i = 0; i < FN; ++i) {
-        const u32x2 v{f32_to_bf16_bits(acc[i][j][0]) | (f32_to_bf16_bits(acc[i][j][1]) << 16),
-                      f32_to_bf16_bits(acc[i][j][2]) | (f32_to_bf16_bits(acc[i][j][3]) << 16)};
-        *reinterpret_cast<u32x2 *>(row + i * 16) = v;
-      }
+      const int piece = ks * 4 + frag_grp;
+      const bool ok = x_off[j] >= 0 && k0 + piece * 8 < k_i;
+      dst[ks][j] = __builtin_bit_cast(
+          bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rsrc, ok ? x_off[j] + piece * 16 : kBig,
+                                                        k0 * 2, 0));
     }
-    return;
-  }
+}
+
+// ---------------------------------------------------------------------------
+// bf16 with X in registers.  Workgroup tile: BN vocabulary rows x WV * TM
+// hidden rows over WV waves; every wave owns all BN rows of W and its own TM
+// hidden rows, so a W element read from LDS feeds TM / 16 MFMAs and an X
+// element held in a register feeds BN / 16 MFMAs.
+//
+// Only W goes through LDS: NS stages of BN x 64 bf16 filled by buffer loads
+// that write LDS directly.  Each wave loads its X fragments straight into
+// registers, already in the MFMA operand layout (lane l: hidden row l % 16,
+// k group l / 16), one register set per step in flight.  W and X of step
+// kt + NS - 1 are issued together at step kt, so NS - 1 whole steps are in
+// flight and the in-order vmcnt count covers both.  Compared with staging X
+// through LDS as well, the same LDS holds three steps of W instead of two,
+// and a W fragment read from LDS feeds the wave's 2 X fragments while each
+// X fragment feeds 20 MFMAs from its register.  Measured on MI355X it is the
+// faster kernel once M spans several 256-row tiles (8-10% over the two-stage
+// kernel at M = 1024 and 4096); at M = 256 the two are even.
+// Requires 16-byte-aligned X and W with K % 8 == 0 (checked by the launcher).
+// ---------------------------------------------------------------------------
+template <int BN, int WV, int TM, int NS, bool GX, bool ARGMAX>
+__global__ __launch_bounds__(WV * 64) void lmhead_bf16_xreg(
+    const uint16_t *__restrict__ X, int64_t M, int64_t K, const uint16_t *__restrict__ W,
+    int64_t N, uint16_t *__restrict__ out, int64_t ld, int64_t col_off, int tiles_n,
+    int tiles_m, int group_n, const int32_t *__restrict__ cu, int64_t n_tokens,
+    ArgmaxOut pick) {
+  // (device pass only: the host pass needs no more than the launch stub)
+#if defined(__HIP_DEVICE_COMPILE__)
+  constexpr int BK = 64, KS = BK / 32;
+  constexpr int FM = TM / 16, BM = WV * TM;
+  constexpr int FN = BN / 16;
+  static_assert(FN * 16 == BN && FM * 16 == TM, "tile sides must be multiples of 16");
+  constexpr int kRowsPerPass = WV * 8;  // one load instruction fills 8 rows
+  static_assert(BN % kRowsPerPass == 0, "W rows must fill whole passes");
+  constexpr int kPPT = BN / kRowsPerPass;  // W loads per lane per step
+  constexpr int kLoadsPerStep = kPPT + KS * FM;
+  constexpr int L = NS - 1;  // steps in flight
+  static_assert(L >= 1 && (L - 1) * kLoadsPerStep <= 63, "vmcnt holds at most 63 loads");
+  __shared__ __attribute__((aligned(16))) uint16_t lds_all[NS * BN * BK];
+  uint16_t(*lds)[BN * BK] = reinterpret_cast<uint16_t(*)[BN * BK]>(lds_all);
+
+  int tn, tm;
+  tile_of_block(blockIdx.x, tiles_n, tiles_m, group_n, tn, tm);
+  const int64_t n0 = static_cast<int64_t>(tn) * BN;
+  const int64_t m0 = static_cast<int64_t>(tm) * BM;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6);
+  const int frag_row = lane & 15, frag_grp = lane >> 4;
+  const int nk = static_cast<int>((K + BK - 1) / BK);
+  const int k_i = static_cast<int>(K);
+  const int row_bytes = static_cast<int>(K * 2);
+  const int w_rows = static_cast<int>((N - n0 < BN) ? N - n0 : BN);
+  const int x_rows = static_cast<int>((M - m0 < BM) ? M - m0 : BM);
+
+  // X rows of this lane's fragments (byte offsets from the X descriptor's
+  // base, -1 for rows that do not exist).  The sequence ends of a gathered X
+  // are loaded first; their first use comes after step 0's W loads are out.
+  int x_off[FM];
+  int32_t cu_end[FM];
 #pragma unroll
   for (int j = 0; j < FM; ++j) {
-    const int64_t m = mb + j * 16;
-    if (m >= M) continue;
-#pragma unroll
-    for (int i = 0; i < FN; ++i) {
-      const int64_t n = nb + i * 16;
-      uint16_t *dst = out + m * ld + col_off + n;
-      if (pack_ok && n + 3 < N) {
-        const u32x2 v{f32_to_bf16_bits(acc[i][j][0]) | (f32_to_bf16_bits(acc[i][j][1]) << 16),
-                      f32_to_bf16_bits(acc[i][j][2]) | (f32_to_bf16_bits(acc[i][j][3]) << 16)};
-        *reinterpret_cast<u32x2 *>(dst) = v;
-      } else {
-        for (int r = 0; r < 4; ++r)
-          if (n + r < N) dst[r] = static_cast<uint16_t>(f32_to_bf16_bits(acc[i][j][r]));
-      }
+    const int r = wave * TM + j * 16 + frag_row;
+    cu_end[j] = 0;
+    if constexpr (GX) {
+      x_off[j] = -1;
+      if (r < x_rows) cu_end[j] = cu[m0 + r + 1];
+    } else {
+      x_off[j] = r < x_rows ? r * row_bytes : -1;
     }
   }
+  // W rows this lane loads: pass p, tile row p * 8 WV + 8 wave + lane / 8,
+  // LDS slot lane % 8 (holding that row's piece slot ^ f(row))
+  const int lrow = lane >> 3, lslot = lane & 7;
+  int w_off[kPPT];
+#pragma unroll
+  for (int p = 0; p < kPPT; ++p) {
+    const int row = p * kRowsPerPass + wave * 8 + lrow;
+    w_off[p] = row < w_rows ? row * row_bytes : -1;
+  }
+  const uint16_t *w_base = W + n0 * K;
+  const int w_bytes = w_rows * row_bytes;
+  const uint16_t *x_base = GX ? X : X + m0 * K;
+  const int x_bytes = static_cast<int>((GX ? n_tokens : x_rows) * K * 2);
+#define VPE_DMA_W(step, buf)                                                                  \
+  xreg_dma_w<kPPT, kRowsPerPass, BK>(w_base, w_bytes, lds[buf], w_off,                       \
+                                     ((step) < nk ? (step) : nk - 1) * BK, k_i, wave, lrow, lslot)
+#define VPE_LOAD_X(step, dst)                                                                 \
+  xreg_load_x<KS, FM>(x_base, x_bytes, dst, x_off, ((step) < nk ? (step) : nk - 1) * BK, k_i, \
+                      frag_grp)
+
+  f32x4 acc[FN][FM];
+#pragma unroll
+  for (int i = 0; i < FN; ++i)
+#pragma unroll
+    for (int j = 0; j < FM; ++j) acc[i][j] = f32x4(0.f);
+  bf16x8 xr[NS][KS][FM];
+
+  VPE_DMA_W(0, 0);
+  if constexpr (GX) {
+#pragma unroll
+    for (int j = 0; j < FM; ++j) {
+      pin_vgpr(cu_end[j]);
+      const int r = wave * TM + j * 16 + frag_row;
+      const int64_t t = static_cast<int64_t>(cu_end[j]) - 1;
+      const bool ok = r < x_rows && static_cast<uint64_t>(t) < static_cast<uint64_t>(n_tokens);
+      x_off[j] = ok ? static_cast<int>(t * K * 2) : -1;
+    }
+  }
+  VPE_LOAD_X(0, xr[0]);
+#pragma unroll
+  for (int st = 1; st < L; ++st) {
+    VPE_DMA_W(st, st);
+    VPE_LOAD_X(st, xr[st]);
+  }
+
+  for (int kb = 0; kb < nk; kb += NS) {
+#pragma unroll
+    for (int u = 0; u < NS; ++u) {
+      if (kb + u >= nk) break;
+      // this wave's W and X of step kb+u have landed once at most the later
+      // L-1 steps' loads are outstanding; the barrier makes every wave's W
+      // visible and closes all reads of the buffer refilled below
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm((L - 1) * kLoadsPerStep));
+      asm volatile("s_barrier" ::: "memory");
+      VPE_DMA_W(kb + u + L, (u + L) % NS);
+      VPE_LOAD_X(kb + u + L, xr[(u + L) % NS]);
+      const uint16_t *cur = lds[u];
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+        for (int i = 0; i < FN; ++i) {
+          const bf16x8 wf = *reinterpret_cast<const bf16x8 *>(
+              cur + lds_piece_offset<BK, 0>(i * 16 + frag_row, ks * 4 + frag_grp));
+#pragma unroll
+          for (int j = 0; j < FM; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf, xr[u][ks][j], acc[i][j], 0,
+                                                                0, 0);
+        }
+      // schedule: the step's loads first, then each W fragment read kAhead
+      // fragments before the MFMAs that use it
+      constexpr int kAhead = 3;
+      __builtin_amdgcn_sched_group_barrier(0x020, kLoadsPerStep, 0);  // buffer loads
+      __builtin_amdgcn_sched_group_barrier(0x100, kAhead, 0);         // LDS reads
+#pragma unroll
+      for (int f = 0; f < KS * FN - kAhead; ++f) {
+        __builtin_amdgcn_sched_group_barrier(0x008, FM, 0);  // MFMAs of fragment f
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // read of fragment f + kAhead
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, kAhead * FM, 0);
+    }
+  }
+#undef VPE_DMA_W
+#undef VPE_LOAD_X
+  // the clamped loads past the last step may still be landing
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+  write_tile<FN, FM, ARGMAX>(acc, n0 + 4 * frag_grp, m0 + wave * TM + frag_row,
+                             n0 + BN <= N && m0 + BM <= M, M, N, out, ld, col_off, pick);
+#endif
 }
 
 // ---------------------------------------------------------------------------
@@ -690,6 +910,42 @@ int launch_bf16_cfg(const uint16_t *x, int64_t m, int64_t k, const uint16_t *w, 
   return 0;
 }
 
+
+// The X-in-registers kernel (see lmhead_bf16_xreg); false when its operand
+// requirements do not hold and the caller must take another kernel.
+template <int BN, int WV, int TM, int NS>
+bool launch_bf16_xreg(const uint16_t *x, int64_t m, int64_t k, const uint16_t *w, int64_t n,
+                      uint16_t *out, int64_t ld, int64_t col_off, hipStream_t st, int group_n,
+                      const int32_t *cu, int64_t n_tokens, ArgmaxOut pick, int *rc) {
+  const bool gx = cu != nullptr;
+  const bool vec = (k % 8 == 0) &&
+                   ((reinterpret_cast<uint64_t>(x) | reinterpret_cast<uint64_t>(w)) & 15) == 0 &&
+                   (gx ? n_tokens * k * 2 <= kBig : int64_t(WV * TM) * k * 2 <= kBig) &&
+                   int64_t(BN) * k * 2 <= kBig;
+  if (!vec) return false;
+  const int64_t tn64 = (n + BN - 1) / BN, tm64 = (m + WV * TM - 1) / (WV * TM);
+  if (tn64 * tm64 > INT32_MAX) {
+    *rc = static_cast<int>(hipErrorInvalidValue);
+    return true;
+  }
+  const int tiles_n = static_cast<int>(tn64), tiles_m = static_cast<int>(tm64);
+  const dim3 grid(static_cast<unsigned>(tiles_n) * static_cast<unsigned>(tiles_m));
+#define VPE_XREG(G, A)                                                                       \
+  hipLaunchKernelGGL((lmhead_bf16_xreg<BN, WV, TM, NS, G, A>), grid, dim3(WV * 64), 0, st, x, m, \
+                     k, w, n, out, ld, col_off, tiles_n, tiles_m, group_n, cu, n_tokens, pick)
+  if (gx) {
+    if (pick.best) VPE_XREG(true, true);
+    else VPE_XREG(true, false);
+  } else {
+    if (pick.best) VPE_XREG(false, true);
+    else VPE_XREG(false, false);
+  }
+#undef VPE_XREG
+  *rc = 0;
+  return true;
+}
+
+
 }  // namespace
 
 int launch_lmhead(const void *x, int64_t m, int64_t k, const void *w, int64_t n, int dtype,
@@ -712,10 +968,13 @@ int launch_lmhead(const void *x, int64_t m, int64_t k, const void *w, int64_t n,
   //  - M <= 64 (decode-size batches): the LM head streams W once and is
   //    bound by HBM; narrow tiles of 128 vocabulary rows keep ~1200 tiles
   //    in flight and four LDS stages keep W loads well ahead of the MFMAs;
-  //  - M > 128: 320 vocabulary rows x 256 hidden rows over 8 waves (a wave
-  //    owns 160 x 64), two LDS stages.  A 75968-row shard is 238 W tiles:
-  //    one round over 256 CUs at M = 256, X re-read once per W tile, and
-  //    0.35 KB of LDS fragment reads per MFMA.
+  //  - 128 < M <= 256: 320 vocabulary rows x 256 hidden rows over 8 waves
+  //    (a wave owns 160 x 64), W and X both staged through two LDS stages.
+  //    A 75968-row shard is 238 W tiles: one round over 256 CUs, with 0.35
+  //    KB of LDS fragment reads per MFMA;
+  //  - M > 256: the same tile with X in registers (lmhead_bf16_xreg), three
+  //    W stages in LDS; tiles ordered in groups of 2 (4 past M = 1024) W
+  //    tiles so that an XCD's concurrent tiles share W and X in its L2.
   int rc;
   if (m <= 16)
     rc = launch_bf16_cfg<Cfg<128, 16, 4, 1, 64, 1, 0, 0, 2, 4>>(xb, m, k, wb, n, ob, ld, col_offset, st, 1, cu, n_tokens, pick);
@@ -725,7 +984,8 @@ int launch_lmhead(const void *x, int64_t m, int64_t k, const void *w, int64_t n,
     rc = launch_bf16_cfg<Cfg<128, 64, 4, 1, 64, 1, 0, 0, 2, 4>>(xb, m, k, wb, n, ob, ld, col_offset, st, 1, cu, n_tokens, pick);
   else if (m <= 128)
     rc = launch_bf16_cfg<Cfg<256, 128, 4, 2, 64, 1, 0, 0, 2, 3>>(xb, m, k, wb, n, ob, ld, col_offset, st, 4, cu, n_tokens, pick);
-  else
+  else if (m <= 256 || !launch_bf16_xreg<320, 8, 32, 3>(xb, m, k, wb, n, ob, ld, col_offset, st,
+                                                       m > 1024 ? 4 : 2, cu, n_tokens, pick, &rc))
     rc = launch_bf16_cfg<Cfg<320, 256, 2, 4, 64, 1, 0, 0, 2, 2>>(xb, m, k, wb, n, ob, ld, col_offset, st, 1, cu, n_tokens, pick);
   if (rc != 0) return rc;
   return static_cast<int>(hipGetLastError());
