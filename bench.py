@@ -55,6 +55,9 @@ def parse_args():
     p.add_argument("--argmax", action="store_true",
                    help="LM head reduced on the fly to each row's greedy pick (largest logit "
                         "and its id) instead of storing the logits")
+    p.add_argument("--lm-rows", type=int, default=0,
+                   help="override the workload's LM-head rows M (decode batch size; "
+                        "not for prefill workloads, whose M is the number of sequences)")
     p.add_argument("--copy-probe-mib", type=int, default=0,
                    help="after timing, run one device-to-device copy of this many MiB "
                         "(a reference kernel for hardware byte counters)")
@@ -128,6 +131,12 @@ def main():
               file=sys.stderr)
         sys.exit(2)
     w = wl.WORKLOADS[args.workload]
+    if args.lm_rows:
+        if w.seqs:
+            print("bench.py: --lm-rows applies to decode workloads only", file=sys.stderr)
+            sys.exit(2)
+        import dataclasses
+        w = dataclasses.replace(w, lm_rows=args.lm_rows)
     dev = torch.device("cuda:0")
     lib = vpe.load_library()
     tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32

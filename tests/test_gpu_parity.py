@@ -542,3 +542,25 @@ def test_parallel_lmhead_layer_fold_argmax():
     ref_max, ref_idx = oracle.argmax_rows(oracle.lmhead_f64(X, full))
     assert np.array_equal(to_host(tok), ref_idx)
     assert np.array_equal(to_host(val).astype(np.float64), ref_max)
+
+
+# ---------------------------------------------------------------------------
+# decode-size LM heads (a handful of rows against a whole shard)
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("m", [1, 2, 5, 8, 16])
+@pytest.mark.parametrize("name", ["qwen3_0p6b_tp1_prefill", "large_v151936_d4096_tp4_rank2"])
+def test_lmhead_decode_rows(name, m):
+    d = _inputs(name)
+    w = d["w"]
+    W = d["shards"][w.ranks[0]]
+    _say(f"lmhead decode {name}: M={m} rows={w.shard_rows} dim={w.dim}")
+    X = wl.hidden_states(600 + m, m, w.dim, w.dtype)
+    x_d, w_d = to_dev(X), to_dev(W)
+    got = to_host(vpe.vpe_lmhead(x_d, w_d))
+    ref = oracle.lmhead_f64(X, W, nthreads=oracle_threads())
+    assert_logits_close(got, ref, f"decode {name} M={m}")
+    # the greedy pick agrees with the stored logits exactly
+    val, tok = _pick(x_d, [w_d], [w.rank_start(w.ranks[0])])
+    g = as_f64(got)
+    assert np.array_equal(tok - w.rank_start(w.ranks[0]), np.argmax(g, axis=1))
+    assert np.array_equal(val, g.max(axis=1))

@@ -125,19 +125,28 @@ __device__ __forceinline__ void write_tile(const f32x4 (&acc)[FN][FM], int64_t n
                                            uint16_t *__restrict__ out, int64_t ld,
                                            int64_t col_off, ArgmaxOut pick) {
   if constexpr (ARGMAX) {
-    // the 4 lanes l, l^16, l^32, l^48 hold the same row m (16 columns each)
+    // the 4 lanes l, l^16, l^32, l^48 hold the same row m (16 columns each).
+    // A lane visits its columns in increasing order and keeps the first
+    // largest bf16 logit, comparing 16-bit order codes (the bf16 analogue of
+    // the key's high word); the 64-bit key is built once per row.
 #pragma unroll
     for (int j = 0; j < FM; ++j) {
       const int64_t m = mb + j * 16;
-      uint64_t key = 0;
+      uint32_t best_ord = 0, best_h = 0;
+      int best_c = -1;  // column offset of the pick inside this lane's columns
 #pragma unroll
       for (int i = 0; i < FN; ++i)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const int64_t n = nb + i * 16 + r;
-          const float v = __uint_as_float(f32_to_bf16_bits(acc[i][j][r]) << 16);
-          if (n < N) key = umax64(key, pick_key(v, pick.id_base + n));
+          const uint32_t h = f32_to_bf16_bits(acc[i][j][r]);
+          const uint32_t ord = (h & 0x8000u) ? (~h & 0xFFFFu) : (h | 0x8000u);
+          const bool take = nb + i * 16 + r < N && (best_c < 0 || ord > best_ord);
+          best_ord = take ? ord : best_ord;
+          best_h = take ? h : best_h;
+          best_c = take ? i * 16 + r : best_c;
         }
+      uint64_t key =
+          best_c < 0 ? 0 : pick_key(__uint_as_float(best_h << 16), pick.id_base + nb + best_c);
       key = umax64(key, __shfl_xor(key, 16));
       key = umax64(key, __shfl_xor(key, 32));
       if ((threadIdx.x & 48) == 0 && m < M)
@@ -967,7 +976,9 @@ int launch_lmhead(const void *x, int64_t m, int64_t k, const void *w, int64_t n,
   // Tile shapes by the number of hidden rows M (measured on MI355X):
   //  - M <= 64 (decode-size batches): the LM head streams W once and is
   //    bound by HBM; narrow tiles of 128 vocabulary rows keep ~1200 tiles
-  //    in flight and four LDS stages keep W loads well ahead of the MFMAs;
+  //    in flight and four LDS stages keep W loads well ahead of the MFMAs
+  //    (M = 1 over 151936 x 1024 runs at 5.8 TB/s); with fewer than 512
+  //    such tiles (long rows, e.g. 37984 x 4096) 64-row tiles take over;
   //  - 128 < M <= 256: 320 vocabulary rows x 256 hidden rows over 8 waves
   //    (a wave owns 160 x 64), W and X both staged through two LDS stages.
   //    A 75968-row shard is 238 W tiles: one round over 256 CUs, with 0.35
@@ -976,7 +987,11 @@ int launch_lmhead(const void *x, int64_t m, int64_t k, const void *w, int64_t n,
   //    W stages in LDS; tiles ordered in groups of 2 (4 past M = 1024) W
   //    tiles so that an XCD's concurrent tiles share W and X in its L2.
   int rc;
-  if (m <= 16)
+  if (m <= 16 && (n + 127) / 128 < 512)
+    // few vocabulary rows (a long K per row): 64-row tiles double the tiles
+    // in flight, 128-wide k steps keep the bytes per stage
+    rc = launch_bf16_cfg<Cfg<64, 16, 4, 1, 128, 1, 0, 0, 2, 6>>(xb, m, k, wb, n, ob, ld, col_offset, st, 1, cu, n_tokens, pick);
+  else if (m <= 16)
     rc = launch_bf16_cfg<Cfg<128, 16, 4, 1, 64, 1, 0, 0, 2, 4>>(xb, m, k, wb, n, ob, ld, col_offset, st, 1, cu, n_tokens, pick);
   else if (m <= 32)
     rc = launch_bf16_cfg<Cfg<128, 32, 4, 1, 64, 1, 0, 0, 2, 4>>(xb, m, k, wb, n, ob, ld, col_offset, st, 1, cu, n_tokens, pick);
