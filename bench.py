@@ -58,6 +58,9 @@ def parse_args():
     p.add_argument("--lm-rows", type=int, default=0,
                    help="override the workload's LM-head rows M (decode batch size; "
                         "not for prefill workloads, whose M is the number of sequences)")
+    p.add_argument("--load-shard", action="store_true",
+                   help="time loading every rank's shard of the workload from the full table "
+                        "on the device (the weight_loader step) instead of the hot path")
     p.add_argument("--copy-probe-mib", type=int, default=0,
                    help="after timing, run one device-to-device copy of this many MiB "
                         "(a reference kernel for hardware byte counters)")
@@ -147,6 +150,9 @@ def main():
         if a.dtype == np.uint16:
             return torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
         return torch.from_numpy(a).to(dev)
+
+    if args.load_shard:
+        return bench_load_shard(args, w, lib, dev, up)
 
     # ---------------- inputs (host, seeded) ----------------
     t0 = time.time()
@@ -361,6 +367,88 @@ def main():
         "roofline": roof,
         "cpu_baseline": cpu,
         "breakdown": breakdown,
+        "device": torch.cuda.get_device_name(dev),
+        "input_gen_s": round(gen_s, 2),
+    }
+    print(json.dumps(line), flush=True)
+
+
+def bench_load_shard(args, w, lib, dev, up):
+    """Every rank's shard copied out of the full [V, D] table on the device
+    (vpe_load_shard); value = algorithmic bytes (read R*D*s + write R*D*s per
+    rank) / step time."""
+    import numpy as np
+    import torch
+
+    import vocab_sharded_embedding_amd as vpe
+    import workloads as wl
+
+    t0 = time.time()
+    full_h = wl.full_table(w)
+    gen_s = time.time() - t0
+    full_d = up(full_h)
+    tdt = full_d.dtype
+    step_bytes = 2 * len(w.ranks) * w.shard_rows * w.dim * w.elem_bytes
+    copies = args.copies or max(1, -(-CACHE_DEFEAT_BYTES // (full_h.nbytes + step_bytes // 2)))
+    fulls = [full_d] + [full_d.clone() for _ in range(copies - 1)]
+    outs = [{r: torch.empty((w.shard_rows, w.dim), dtype=tdt, device=dev) for r in w.ranks}
+            for _ in range(copies)]
+    dcode = vpe.VPE_BF16 if w.dtype == "bf16" else vpe.VPE_F32
+    stream = torch.cuda.current_stream(dev)
+    sh = stream.cuda_stream
+    calls = [[(lib.vpe_load_shard, (fulls[c].data_ptr(), w.vocab, w.dim, dcode, w.tp, r,
+                                    outs[c][r].data_ptr(), sh)) for r in w.ranks]
+             for c in range(copies)]
+
+    def run_step(k, evs=None):
+        for j, (fn, a) in enumerate(calls[k % copies]):
+            if evs is not None:
+                evs[j][0].record(stream)
+            rc = fn(*a)
+            if evs is not None:
+                evs[j][1].record(stream)
+            if rc != 0:
+                raise RuntimeError(f"load_shard failed: {vpe.status_name(rc)}")
+
+    with torch.cuda.stream(stream):
+        for k in range(args.warmup):
+            run_step(k)
+        evs = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                for _ in w.ranks] for _ in range(args.steps)]
+        torch.cuda.synchronize()
+        t_start = time.perf_counter()
+        for k in range(args.steps):
+            run_step(k, evs[k])
+        torch.cuda.synchronize()
+        t_total = time.perf_counter() - t_start
+    us = [float(np.mean([evs[k][j][0].elapsed_time(evs[k][j][1]) for k in range(args.steps)])) * 1e3
+          for j in range(len(w.ranks))]
+    per_launch = step_bytes / len(w.ranks)
+    ms_per_step = t_total * 1e3 / args.steps
+    value = step_bytes / (ms_per_step * 1e-3) / 1e9
+    ach = per_launch / (float(np.mean(us)) * 1e-6) / 1e9
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        t0 = time.perf_counter()
+        for r in w.ranks:
+            oracle.load_shard(full_h, w.tp, r)
+        dt = time.perf_counter() - t0
+        cpu = {"value": round(step_bytes / dt / 1e9, 3), "unit": "GB/s", "cores": 1,
+               "kind": "oracle", "sample": f"every rank's shard once; {dt:.2f} s wall"}
+    line = {
+        "metric": "shard load GB/s (read + write of every rank's rows)", "value": round(value, 2),
+        "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": w.dtype, "data": "synthetic",
+        "config": {"workload": w.name + "/load_shard", "vocab": w.vocab, "dim": w.dim, "tp": w.tp,
+                   "ranks": list(w.ranks), "rotating_copies": copies,
+                   "step_algorithmic_bytes": step_bytes},
+        "roofline": {"kernel": "load_shard", "bound": "hbm", "achieved": round(ach, 1),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4),
+                     "traffic": None, "algorithmic_bytes_per_launch": per_launch,
+                     "avg_launch_us": round(float(np.mean(us)), 3)},
+        "cpu_baseline": cpu,
         "device": torch.cuda.get_device_name(dev),
         "input_gen_s": round(gen_s, 2),
     }

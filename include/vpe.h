@@ -199,6 +199,24 @@ vpe_status vpe_lmhead_prefill(const void *hidden, int64_t n_tokens, int64_t dim,
                               int64_t col_offset, void *stream);
 
 /*
+ * One rank's shard of the full table, loaded on the device: the rank keeps
+ * rows [tp_rank * R, tp_rank * R + R) of the [vocab, dim] table, R = vocab /
+ * tp_size ([TP-vocab] section 3 weight_loader: narrow along the vocabulary
+ * dimension, then copy into the parameter; [vLLM-1.1] source analysis).
+ *   full   device [vocab, dim] row-major, dtype dt (read only)
+ *   shard  device [R, dim] row-major, written; must not overlap the rows
+ *          copied from `full`
+ * Element bits are copied unchanged.  The same shard serves vpe_embed and
+ * vpe_lmhead (tied tables, [Guide-3.3] section 8).
+ * Errors: VPE_ERR_DTYPE, VPE_ERR_SHAPE (vocab or dim < 1, too large),
+ * VPE_ERR_SHARD (vocab % tp_size != 0, rank out of range), VPE_ERR_NULL,
+ * VPE_ERR_ALIGN (pointers not aligned to the element size), VPE_ERR_RANGE
+ * (shard overlaps its source rows).
+ */
+vpe_status vpe_load_shard(const void *full, int64_t vocab, int64_t dim, vpe_dtype dt,
+                          int32_t tp_size, int32_t tp_rank, void *shard, void *stream);
+
+/*
  * Greedy pick over the vocabulary without materialising the logits.  The
  * full-vocabulary logits exist to feed the sampler ([TP-vocab] section 4:
  * each rank's shard of the logits is gathered and concatenated; [Guide-3.3]

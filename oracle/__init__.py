@@ -63,6 +63,8 @@ def _load():
         lib.orc_lmhead_f64.argtypes = [vp, i64, i64, vp, i64, ci, vp, i64, i64, ci]
         lib.orc_logit_f64.argtypes = [vp, i64, vp, ci, i64, i64]
         lib.orc_argmax_rows.argtypes = [vp, i64, i64, i64, vp, vp]
+        lib.orc_load_shard.argtypes = [vp, i64, i64, ci, i32, i32, vp]
+        lib.orc_load_shard.restype = ci
         lib.orc_argmax_rows.restype = ci
         lib.orc_logit_f64.restype = ctypes.c_double
         lib.orc_round_bf16.argtypes = [ctypes.c_float]
@@ -112,6 +114,19 @@ def shard_range(vocab: int, tp_size: int, tp_rank: int) -> Tuple[int, int]:
     _check(lib.orc_shard_range(vocab, tp_size, tp_rank, ctypes.byref(s), ctypes.byref(e)),
            "shard_range")
     return s.value, e.value
+
+
+def load_shard(full: np.ndarray, tp_size: int, tp_rank: int) -> np.ndarray:
+    """Rows [rank*R, rank*R + R) of the full [V, D] table, bits unchanged."""
+    full = np.ascontiguousarray(full)
+    if full.ndim != 2:
+        raise ValueError("full table must be [V, D]")
+    vocab, dim = full.shape
+    rows = vocab // tp_size if tp_size > 0 else 0
+    out = np.empty((rows, dim), dtype=full.dtype)
+    _check(_load().orc_load_shard(_ptr(full), vocab, dim, _dtype_code(full), tp_size, tp_rank,
+                                  _ptr(out)), "load_shard")
+    return out
 
 
 def mask_shift(ids: np.ndarray, vocab_start: int, vocab_end: int):

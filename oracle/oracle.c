@@ -103,6 +103,25 @@ int orc_shard_range(int64_t vocab, int32_t tp_size, int32_t tp_rank,
 }
 
 /* ------------------------------------------------------------------ */
+/* shard loading: [TP-vocab] section 3 weight_loader, [vLLM-1.1] source */
+/* analysis: a rank keeps rows [rank*R, rank*R + R) of the full [V, D]  */
+/* table (narrow along dim 0, then copy), element bits unchanged.       */
+/* ------------------------------------------------------------------ */
+int orc_load_shard(const void *full, int64_t vocab, int64_t dim, int dtype, int32_t tp_size,
+                   int32_t tp_rank, void *shard) {
+    int64_t start, end;
+    int rc = orc_shard_range(vocab, tp_size, tp_rank, &start, &end);
+    if (rc != ORC_OK) return rc;
+    if (dim < 1 || (dtype != ORC_F32 && dtype != ORC_BF16)) return ORC_ERR_ARG;
+    if (!full || !shard) return ORC_ERR_ARG;
+    const int64_t row_bytes = dim * orc_elem_bytes(dtype);
+    for (int64_t r = start; r < end; ++r)
+        memcpy((char *)shard + (r - start) * row_bytes, (const char *)full + r * row_bytes,
+               (size_t)row_bytes);
+    return ORC_OK;
+}
+
+/* ------------------------------------------------------------------ */
 /* steps 1-2 of the masked lookup ([TP-vocab] section 3, [vLLM-1.1]     */
 /* steps 1 and 2): mask = start <= x < end; local = mask ? x-start : 0  */
 /* ------------------------------------------------------------------ */

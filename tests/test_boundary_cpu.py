@@ -26,7 +26,7 @@ def test_header_declares_the_calls():
     assert _declared() == sorted(["vpe_shard_range", "vpe_embed", "vpe_sum_partials",
                                   "vpe_last_token_select", "vpe_lmhead", "vpe_lmhead_prefill",
                                   "vpe_argmax_init", "vpe_lmhead_argmax", "vpe_argmax_decode",
-                                  "vpe_status_string"])
+                                  "vpe_load_shard", "vpe_status_string"])
 
 
 def test_library_exports_every_declared_symbol():
@@ -212,3 +212,22 @@ def test_argmax_validation():
     assert lib.vpe_argmax_init(FAKE, 2 ** 21 + 1, None) == vpe.VPE_ERR_SHAPE
     assert d(FAKE, 2 ** 21 + 1, FAKE, FAKE, None) == vpe.VPE_ERR_SHAPE
     assert f(FAKE, 2 ** 21 + 1, 64, FAKE, 100, BF16, 0, FAKE, None) == vpe.VPE_ERR_SHAPE
+
+
+def test_load_shard_validation():
+    lib = vpe.load_library()
+    f = lib.vpe_load_shard
+    assert f(FAKE, 100, 8, 9, 2, 0, FAKE + 4096, None) == vpe.VPE_ERR_DTYPE
+    assert f(FAKE, 100, 0, BF16, 2, 0, FAKE + 4096, None) == vpe.VPE_ERR_SHAPE
+    assert f(FAKE, 0, 8, BF16, 2, 0, FAKE + 4096, None) == vpe.VPE_ERR_SHAPE
+    assert f(FAKE, 2 ** 40, 2 ** 10, BF16, 2, 0, FAKE + 4096, None) == vpe.VPE_ERR_SHAPE
+    assert f(FAKE, 101, 8, BF16, 2, 0, FAKE + 4096, None) == vpe.VPE_ERR_SHARD
+    assert f(FAKE, 100, 8, BF16, 2, 2, FAKE + 4096, None) == vpe.VPE_ERR_SHARD
+    assert f(FAKE, 100, 8, BF16, 0, 0, FAKE + 4096, None) == vpe.VPE_ERR_SHARD
+    assert f(None, 100, 8, BF16, 2, 0, FAKE + 4096, None) == vpe.VPE_ERR_NULL
+    assert f(FAKE, 100, 8, BF16, 2, 0, None, None) == vpe.VPE_ERR_NULL
+    assert f(FAKE + 1, 100, 8, BF16, 2, 0, FAKE + 4096, None) == vpe.VPE_ERR_ALIGN
+    assert f(FAKE, 100, 8, F32, 2, 0, FAKE + 4098, None) == vpe.VPE_ERR_ALIGN
+    # rank 1's rows start at byte 50*8*2 = 800: a shard at FAKE + 1000 overlaps them
+    assert f(FAKE, 100, 8, BF16, 2, 1, FAKE + 1000, None) == vpe.VPE_ERR_RANGE
+    assert f(FAKE, 100, 8, BF16, 2, 0, FAKE + 16, None) == vpe.VPE_ERR_RANGE

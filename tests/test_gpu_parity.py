@@ -564,3 +564,56 @@ def test_lmhead_decode_rows(name, m):
     g = as_f64(got)
     assert np.array_equal(tok - w.rank_start(w.ranks[0]), np.argmax(g, axis=1))
     assert np.array_equal(val, g.max(axis=1))
+
+
+# ---------------------------------------------------------------------------
+# shard loading on the device, and one tied table for both calls
+# ---------------------------------------------------------------------------
+def test_load_shard_full_vocab_every_rank():
+    d = _inputs("qwen3_0p6b_tp1_prefill")  # its only shard is the full 151936 x 1024 table
+    full = d["shards"][0]
+    full_d = to_dev(full)
+    for tp in (2, 4):
+        for r in range(tp):
+            _say(f"load_shard full table tp={tp} rank={r}")
+            got = to_host(vpe.vpe_load_shard(full_d, tp, r))
+            assert got.tobytes() == oracle.load_shard(full, tp, r).tobytes(), (tp, r)
+
+
+@pytest.mark.parametrize("dtype,vocab,dim", [("f32", 12, 3), ("f32", 96, 5), ("bf16", 30, 7),
+                                             ("bf16", 64, 8), ("bf16", 4096, 1000),
+                                             ("f32", 6, 1)])
+def test_load_shard_odd_rows(dtype, vocab, dim):
+    # rows whose byte length is not a multiple of 16: shard starts and ends fall
+    # off 16-byte boundaries (bytewise path) or leave a tail after the vectors
+    full = wl.table_rows(700 + vocab, vocab, dim, dtype, 0, vocab)
+    full_d = to_dev(full)
+    for tp in [t for t in (1, 2, 3, 4, 6) if vocab % t == 0]:
+        for r in range(tp):
+            out = torch.full((vocab // tp, dim), -1536.0, dtype=full_d.dtype, device=dev())
+            vpe.vpe_load_shard(full_d, tp, r, out=out)
+            assert to_host(out).tobytes() == oracle.load_shard(full, tp, r).tobytes()
+
+
+def test_weight_loader_and_tied_head():
+    V, D, tp = 1024, 96, 4
+    full = wl.table_rows(710, V, D, "bf16", 0, V)
+    full_d = to_dev(full)
+    ids = wl.token_ids(711, V, 300)
+    X = wl.hidden_states(712, 7, D, "bf16")
+    parts = []
+    logits = torch.empty((7, V), dtype=torch.bfloat16, device=dev())
+    for r in range(tp):
+        emb = vpe.VocabParallelEmbedding(V, D, tp_size=tp, tp_rank=r, device=dev())
+        emb.weight_loader(emb.weight, full_d)  # device table: the library's copy kernel
+        assert to_host(emb.weight.data).tobytes() == oracle.load_shard(full, tp, r).tobytes()
+        head = vpe.ParallelLMHead(V, D, tp_size=tp, tp_rank=r, device=dev()).tie_to(emb)
+        assert head.weight.data_ptr() == emb.weight.data_ptr()
+        parts.append(emb(to_dev(ids)))
+        head(to_dev(X), logits=logits)
+    total = to_host(vpe.VocabParallelEmbedding.sum_partials(parts))
+    assert total.tobytes() == oracle.embed(ids, full, 0).tobytes()
+    assert_logits_close(to_host(logits), oracle.lmhead_f64(X, full), "tied heads")
+    with pytest.raises(ValueError):
+        vpe.ParallelLMHead(V, D, tp_size=tp, tp_rank=0, device=dev()).tie_to(
+            vpe.VocabParallelEmbedding(V, D, tp_size=tp, tp_rank=1, device=dev()))

@@ -348,3 +348,35 @@ def test_argmax_of_concatenated_shards_is_global_argmax():
     best = [max((oracle.argmax_rows(cat[:, s:e])[0][m], -(oracle.argmax_rows(cat[:, s:e])[1][m] + s))
                 for s, e in (oracle.shard_range(V, tp, r) for r in range(tp))) for m in range(M)]
     assert [-b[1] for b in best] == list(oracle.argmax_rows(full)[1])
+
+
+# ---------------------------------------------------------------------------
+# shard loading (each rank's weight_loader keeps rows [rank*R, rank*R + R))
+# ---------------------------------------------------------------------------
+def test_load_shard_arange_4x2_demo():
+    g = _golden("tpvocab_arange_4x2.json")
+    full = np.arange(1, 9, dtype=np.float32).reshape(4, 2)
+    for rank in range(2):
+        assert oracle.load_shard(full, 2, rank).tolist() == g["derived_by_hand"][f"rank{rank}_shard"]
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_load_shard_is_numpy_slice_and_shards_tile_the_table(dtype):
+    for vocab, dim in [(1, 1), (12, 4), (96, 3), (1000, 40)]:
+        full = wl.table_rows(70 + vocab, vocab, dim, dtype, 0, vocab)
+        for tp in [t for t in range(1, 9) if vocab % t == 0]:
+            shards = []
+            for rank in range(tp):
+                sh = oracle.load_shard(full, tp, rank)
+                r = vocab // tp
+                assert sh.tobytes() == full[rank * r:(rank + 1) * r].tobytes()
+                shards.append(sh)
+            assert np.concatenate(shards).tobytes() == full.tobytes()
+
+
+def test_load_shard_rejects_uneven_split():
+    full = np.zeros((10, 4), np.float32)
+    with pytest.raises(oracle.OracleError):
+        oracle.load_shard(full, 3, 0)
+    with pytest.raises(oracle.OracleError):
+        oracle.load_shard(full, 2, 2)

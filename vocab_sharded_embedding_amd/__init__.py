@@ -28,7 +28,7 @@ VPE_MAX_PARTS = 64
 EXPORTED_SYMBOLS = ("vpe_shard_range", "vpe_embed", "vpe_sum_partials",
                     "vpe_last_token_select", "vpe_lmhead", "vpe_lmhead_prefill",
                     "vpe_argmax_init", "vpe_lmhead_argmax", "vpe_argmax_decode",
-                    "vpe_status_string")
+                    "vpe_load_shard", "vpe_status_string")
 
 
 class VpeError(RuntimeError):
@@ -62,6 +62,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.vpe_argmax_init.argtypes = [vp, i64, vp]
     lib.vpe_lmhead_argmax.argtypes = [vp, i64, i64, vp, i64, ci, i64, vp, vp]
     lib.vpe_argmax_decode.argtypes = [vp, i64, vp, vp, vp]
+    lib.vpe_load_shard.argtypes = [vp, i64, i64, ci, ctypes.c_int32, ctypes.c_int32, vp, vp]
     for name in EXPORTED_SYMBOLS[:-1]:
         getattr(lib, name).restype = ci
     lib.vpe_status_string.argtypes = [ci]
@@ -259,6 +260,29 @@ def vpe_lmhead_prefill(hidden, cu_seqlens, weight, logits=None, col_offset: int 
     return logits
 
 
+def vpe_load_shard(full, tp_size: int, tp_rank: int, out=None):
+    """Rows [rank*R, rank*R + R) of the device table `full` [V, D] into `out` [R, D]."""
+    torch = _torch()
+    _need_device("full", full)
+    if full.dim() != 2 or not full.is_contiguous():
+        raise ValueError("full must be a contiguous [V, D] tensor")
+    vocab, dim = full.shape
+    if tp_size < 1 or vocab % tp_size != 0:
+        raise ValueError(f"vocab {vocab} does not split evenly over tp_size {tp_size}")
+    rows = vocab // tp_size
+    if out is None:
+        out = torch.empty((rows, dim), dtype=full.dtype, device=full.device)
+    else:
+        _need_device("out", out)
+        if tuple(out.shape) != (rows, dim) or out.dtype != full.dtype or not out.is_contiguous():
+            raise ValueError("out must be a contiguous [V/tp, D] tensor of the table's dtype")
+        _same_device(full, out)
+    _check("vpe_load_shard", load_library().vpe_load_shard(
+        full.data_ptr(), vocab, dim, _dtype_code(full), tp_size, tp_rank, out.data_ptr(),
+        _stream_handle(full.device)))
+    return out
+
+
 def vpe_argmax_init(best):
     """Reset the [m] uint64 (int64 tensor) greedy-pick keys to 0."""
     torch = _torch()
@@ -308,5 +332,6 @@ from .layers import ParallelLMHead, VocabParallelEmbedding  # noqa: E402
 __all__ = [
     "vpe_shard_range", "vpe_embed", "vpe_sum_partials", "vpe_last_token_select", "vpe_lmhead",
     "vpe_lmhead_prefill", "vpe_argmax_init", "vpe_lmhead_argmax", "vpe_argmax_decode",
+    "vpe_load_shard",
     "VocabParallelEmbedding", "ParallelLMHead", "VpeError", "load_library", "LIB_PATH",
 ]

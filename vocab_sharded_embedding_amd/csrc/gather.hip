@@ -21,6 +21,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <algorithm>
+
 #include "vpe_launch.h"
 
 namespace vpe {
@@ -286,7 +288,55 @@ void launch_sum_range(const PartList &pl, int n_parts, int64_t e0, int64_t e1, v
                      e0, e1, out);
 }
 
+// Contiguous copy (a rank's rows of the full table are one contiguous block).
+// 16-byte vectors, two in flight per thread, grid-stride over the vectors;
+// the tail (and any copy whose ends are not 16-byte aligned) goes bytewise.
+// Measured on MI355X for a 311 MB copy: two vectors per thread over 8192
+// blocks reach 5.9 TB/s; four per thread over 4096 blocks 4.8 TB/s.
+__global__ __launch_bounds__(kBlock) void copy_vec_kernel(const u32x4 *__restrict__ src,
+                                                          u32x4 *__restrict__ dst, int64_t n_vec) {
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * kBlock;
+  int64_t i = static_cast<int64_t>(blockIdx.x) * kBlock + threadIdx.x;
+  for (; i + stride < n_vec; i += 2 * stride) {
+    const u32x4 a = __builtin_nontemporal_load(src + i);
+    const u32x4 b = __builtin_nontemporal_load(src + i + stride);
+    __builtin_nontemporal_store(a, dst + i);
+    __builtin_nontemporal_store(b, dst + i + stride);
+  }
+  if (i < n_vec) __builtin_nontemporal_store(__builtin_nontemporal_load(src + i), dst + i);
+}
+
+__global__ __launch_bounds__(kBlock) void copy_bytes_kernel(const uint8_t *__restrict__ src,
+                                                            uint8_t *__restrict__ dst, int64_t n) {
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * kBlock;
+  for (int64_t i = static_cast<int64_t>(blockIdx.x) * kBlock + threadIdx.x; i < n; i += stride)
+    dst[i] = src[i];
+}
+
 }  // namespace
+
+int launch_copy_bytes(const void *src, void *dst, int64_t n_bytes, void *stream) {
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  (void)hipGetLastError();  // clear a stale error so the status returned is this launch's
+  const uint8_t *s8 = static_cast<const uint8_t *>(src);
+  uint8_t *d8 = static_cast<uint8_t *>(dst);
+  const bool aligned16 =
+      ((reinterpret_cast<uint64_t>(src) | reinterpret_cast<uint64_t>(dst)) & 15) == 0;
+  const int64_t n_vec = aligned16 ? n_bytes / 16 : 0;
+  constexpr int64_t kMaxBlocks = 8192;  // 32 per CU; the loops stride over the rest
+  if (n_vec > 0) {
+    const int64_t blocks = std::min<int64_t>((n_vec + 2 * kBlock - 1) / (2 * kBlock), kMaxBlocks);
+    hipLaunchKernelGGL(copy_vec_kernel, dim3(static_cast<unsigned>(blocks)), dim3(kBlock), 0, st,
+                       reinterpret_cast<const u32x4 *>(s8), reinterpret_cast<u32x4 *>(d8), n_vec);
+  }
+  const int64_t rest = n_bytes - n_vec * 16;
+  if (rest > 0) {
+    const int64_t blocks = std::min<int64_t>((rest + kBlock - 1) / kBlock, kMaxBlocks);
+    hipLaunchKernelGGL(copy_bytes_kernel, dim3(static_cast<unsigned>(blocks)), dim3(kBlock), 0, st,
+                       s8 + n_vec * 16, d8 + n_vec * 16, rest);
+  }
+  return static_cast<int>(hipGetLastError());
+}
 
 int launch_embed(const void *ids, int itype, int64_t n, const void *weight, int64_t shard_rows,
                  int64_t row_bytes, int64_t vocab_start, void *out, void *stream) {

@@ -132,6 +132,25 @@ vpe_status vpe_lmhead_prefill(const void *hidden, int64_t n_tokens, int64_t dim,
                                      cu_seqlens, n_tokens));
 }
 
+vpe_status vpe_load_shard(const void *full, int64_t vocab, int64_t dim, vpe_dtype dt,
+                          int32_t tp_size, int32_t tp_rank, void *shard, void *stream) {
+  if (!known_dtype(dt)) return VPE_ERR_DTYPE;
+  if (dim < 1 || vocab < 1 || vocab > kMaxElems / dim) return VPE_ERR_SHAPE;
+  int64_t start = 0, end = 0;
+  const vpe_status rs = vpe_shard_range(vocab, tp_size, tp_rank, &start, &end);
+  if (rs != VPE_OK) return rs;
+  if (!full || !shard) return VPE_ERR_NULL;
+  const int64_t row_bytes = dim * dtype_bytes(dt);
+  const char *src = static_cast<const char *>(full) + start * row_bytes;
+  const int64_t n_bytes = (end - start) * row_bytes;
+  if (!aligned(full, dtype_bytes(dt)) || !aligned(shard, dtype_bytes(dt))) return VPE_ERR_ALIGN;
+  // the shard must not overlap the rows it is copied from
+  const uintptr_t s0 = reinterpret_cast<uintptr_t>(src), d0 = reinterpret_cast<uintptr_t>(shard);
+  const uintptr_t nb = static_cast<uintptr_t>(n_bytes);
+  if (d0 < s0 + nb && s0 < d0 + nb) return VPE_ERR_RANGE;
+  return launched(vpe::launch_copy_bytes(src, shard, n_bytes, stream));
+}
+
 vpe_status vpe_argmax_init(uint64_t *best, int64_t m, void *stream) {
   if (m < 0 || m > (int64_t(1) << 21)) return VPE_ERR_SHAPE;
   if (m == 0) return VPE_OK;

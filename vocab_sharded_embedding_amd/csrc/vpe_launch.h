@@ -21,6 +21,9 @@ int launch_last_token_select(const void *hidden, int64_t n_tokens, int64_t row_b
                              const int32_t *cu_seqlens, int64_t n_seqs, void *out,
                              void *stream);
 
+// dst[0, n_bytes) = src[0, n_bytes) (non-overlapping device buffers).
+int launch_copy_bytes(const void *src, void *dst, int64_t n_bytes, void *stream);
+
 // out = sum of n_parts partials in rank order (fp32 adds, one rounding).
 // dtype: 0 = f32, 1 = bf16.  n_parts in [1, 64].
 int launch_sum_partials(const void *const *parts, int n_parts, int64_t n_elems, int dtype,

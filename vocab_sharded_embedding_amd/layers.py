@@ -17,8 +17,8 @@ from typing import Optional, Sequence
 
 import torch
 
-from . import (vpe_embed, vpe_lmhead, vpe_lmhead_argmax, vpe_lmhead_prefill, vpe_shard_range,
-               vpe_sum_partials)
+from . import (vpe_embed, vpe_lmhead, vpe_lmhead_argmax, vpe_lmhead_prefill, vpe_load_shard,
+               vpe_shard_range, vpe_sum_partials)
 
 
 class VocabParallelEmbedding(torch.nn.Module):
@@ -40,8 +40,19 @@ class VocabParallelEmbedding(torch.nn.Module):
         self.weight.weight_loader = self.weight_loader
 
     def weight_loader(self, param: torch.nn.Parameter, loaded_weight: torch.Tensor) -> None:
-        """Copy this rank's rows of the full [V, D] table into the shard (setup only)."""
+        """Copy this rank's rows of the full [V, D] table into the shard (setup only).
+
+        A full table already on the shard's device is copied by the library's
+        own kernel (`vpe_load_shard`); a host table (e.g. read from disk) is
+        narrowed and uploaded.
+        """
         shard = param.data.size(0)
+        full_shape = (self.num_embeddings, self.embedding_dim)
+        if (loaded_weight.device == param.data.device and loaded_weight.is_cuda
+                and tuple(loaded_weight.shape) == full_shape and loaded_weight.is_contiguous()
+                and loaded_weight.dtype == param.data.dtype):
+            vpe_load_shard(loaded_weight, self.tp_size, self.tp_rank, out=param.data)
+            return
         piece = loaded_weight.narrow(0, self.tp_rank * shard, shard)
         if piece.shape != param.data.shape:
             raise ValueError(f"loaded table slice {tuple(piece.shape)} does not match "
@@ -60,6 +71,17 @@ class VocabParallelEmbedding(torch.nn.Module):
 
 
 class ParallelLMHead(VocabParallelEmbedding):
+    def tie_to(self, embedding: VocabParallelEmbedding) -> "ParallelLMHead":
+        """Share the embedding's shard as this head's weight (tied tables,
+        AIInfraGuide 3.3 section 8): one [V/tp, D] buffer serves both calls."""
+        same = (embedding.num_embeddings, embedding.embedding_dim, embedding.tp_size,
+                embedding.tp_rank) == (self.num_embeddings, self.embedding_dim, self.tp_size,
+                                       self.tp_rank)
+        if not same:
+            raise ValueError("a tied head needs the embedding's vocabulary, width and rank")
+        self.weight = embedding.weight
+        return self
+
     def forward(self, hidden: torch.Tensor, cu_seqlens: Optional[torch.Tensor] = None,
                 logits: Optional[torch.Tensor] = None) -> torch.Tensor:
         """This rank's logits.
