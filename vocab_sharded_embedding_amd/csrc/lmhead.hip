@@ -73,19 +73,18 @@ __device__ __forceinline__ void pin_vgpr(int32_t &v) { asm volatile("" : "+v"(v)
 // bytes), and the 8 lanes of a pass read the same piece of 8 consecutive
 // rows.  Piece p of row r is stored at slot p ^ f(r) with
 //   f(r) = (r / G) mod P,   G = rows per 128 bytes (2 for BK = 32, else 1),
-// so those 8 rows' pieces land in 8 distinct 16-byte bank groups
-// (SWZ 1: f(r) = (r / 2) mod P for every BK, kept for measurements).
+// so those 8 rows' pieces land in 8 distinct 16-byte bank groups.
 // ---------------------------------------------------------------------------
-template <int BK, int SWZ>
+template <int BK>
 __device__ __forceinline__ int lds_swizzle(int row) {
   constexpr int P = BK / 8;
-  constexpr int G = (SWZ == 1) ? 2 : ((BK * 2 >= 128) ? 1 : 128 / (BK * 2));
+  constexpr int G = (BK * 2 >= 128) ? 1 : 128 / (BK * 2);
   return (row / G) & (P - 1);
 }
 
-template <int BK, int SWZ>
+template <int BK>
 __device__ __forceinline__ int lds_piece_offset(int row, int piece) {
-  return row * BK + ((piece ^ lds_swizzle<BK, SWZ>(row)) << 3);  // in bf16 elements
+  return row * BK + ((piece ^ lds_swizzle<BK>(row)) << 3);  // in bf16 elements
 }
 
 // Workgroup tile order.  Work-groups are handed to the 8 XCDs round-robin
@@ -275,41 +274,29 @@ __device__ __forceinline__ void write_tile_lds(const f32x4 (&acc)[FN][FM], uint1
 
 // Tile configuration of the bf16 kernel.
 //   BN x BM   tile of Z^T per workgroup (BN vocabulary rows of W, BM rows of X)
-//   WN x WM   arrangement of the 4 waves; a wave owns (BN/WN) x (BM/WM)
+//   WN x WM   arrangement of the waves; a wave owns (BN/WN) x (BM/WM)
 //   BK        K slice per pipeline step (64 or 128)
-//   PF        register sets for staged global data (loads run ahead by
-//             max(PF, 2) steps: 1 set = the next step's loads are issued
-//             halfway through the current step's MFMAs)
-//   SWZ       LDS swizzle variant (see lds_piece_offset)
-//   RS        fragment read schedule: 0 = every fragment of a step read
-//             before its first MFMA; 1 = the second 32-wide half's fragments
-//             are read while the first half's MFMAs run (fewer live registers)
-//   PIPE      0: two LDS buffers, a step's fragments are read after the
-//             barrier that opens it; 1: three LDS buffers and two fragment
-//             register sets, so a step's MFMAs use fragments read during the
-//             previous step and never wait on LDS after a barrier;
-//             2: NS LDS stages filled by buffer loads that write LDS directly
-//             (no staging registers), NS-1 steps in flight
-//   NS        LDS stages of PIPE 2
+//   NS        LDS stages (filled by buffer loads that write LDS directly;
+//             NS-1 steps in flight)
 // The workgroup has WN * WM waves of 64 lanes.
-template <int BN_, int BM_, int WN_, int WM_, int BK_, int PF_, int SWZ_ = 0, int RS_ = 0,
-          int PIPE_ = 0, int NS_ = 3>
+template <int BN_, int BM_, int WN_, int WM_, int BK_, int NS_>
 struct Cfg {
-  static constexpr int BN = BN_, BM = BM_, WN = WN_, WM = WM_, BK = BK_, PF = PF_, SWZ = SWZ_;
-  static constexpr int RS = RS_, PIPE = PIPE_, NS = NS_;
+  static constexpr int BN = BN_, BM = BM_, WN = WN_, WM = WM_, BK = BK_, NS = NS_;
   static constexpr int NT = WN_ * WM_ * 64;
+  static_assert(NS >= 2, "at least two LDS stages");
 };
 
 // s_waitcnt immediate that waits until at most n vector-memory operations of
 // this wave are outstanding (LDS and export counters left alone).
 constexpr int vmcnt_imm(int n) { return (n & 0xF) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8); }
 
-// Z^T tile = W_tile . X_tile^T over K, staged through two LDS buffers.
-// Each step: barrier; read every MFMA fragment of step k from one buffer;
-// write step k+1 (already in registers) to the other buffer; issue the
-// global loads of a later step; run the MFMAs.  One barrier per step, and
-// the LDS writes and global loads overlap the MFMAs.  In LDS, rows [0, BN)
-// hold the W slice and rows [BN, BN+BM) the X slice of a step.
+// Z^T tile = W_tile . X_tile^T over K, staged through LDS.  In LDS, rows
+// [0, BN) of a stage hold the W slice and rows [BN, BN+BM) the X slice of a
+// step.  VEC (16-byte-aligned operands, K % 8 == 0): NS stages filled by
+// buffer loads that write LDS directly, NS-1 steps in flight, one barrier per
+// step.  Otherwise: two stages, element-wise loads staged through registers
+// (each step: barrier; read the step's fragments; write the next step from
+// registers to the other stage; issue the loads of the step after; MFMAs).
 //
 // GX (prefill): the M rows of X are not stored contiguously; row i is the
 // last position of packed sequence i, hidden[cu[i+1] - 1] with hidden
@@ -322,8 +309,8 @@ __global__ __launch_bounds__(C::NT) void lmhead_bf16_mfma(
     int64_t N, uint16_t *__restrict__ out, int64_t ld, int64_t col_off, int tiles_n,
     int tiles_m, int group_n, const int32_t *__restrict__ cu, int64_t n_tokens,
     ArgmaxOut pick) {
-  constexpr int BN = C::BN, BM = C::BM, WN = C::WN, WM = C::WM, BK = C::BK, PF = C::PF;
-  constexpr int SWZ = C::SWZ, RS = C::RS, NT = C::NT, PIPE = C::PIPE;
+  constexpr int BN = C::BN, BM = C::BM, WN = C::WN, WM = C::WM, BK = C::BK;
+  constexpr int NT = C::NT;
   constexpr int TN = BN / WN, TM = BM / WM;
   constexpr int FN = TN / 16, FM = TM / 16;
   static_assert(FN * 16 == TN && FM * 16 == TM, "wave tile must be a multiple of 16");
@@ -333,9 +320,9 @@ __global__ __launch_bounds__(C::NT) void lmhead_bf16_mfma(
   constexpr int kPPT = (kRows + kRowsPerPass - 1) / kRowsPerPass;  // pieces per thread
   constexpr int KS = BK / 32;                      // MFMA k-steps per pipeline step
 
-  // PIPE 2 pads a stage to whole passes: every lane of a load writes inside it
-  constexpr int kNumBuf = PIPE == 2 ? C::NS : (PIPE ? 3 : 2);
-  constexpr int kBufElems = (PIPE == 2 ? kPPT * kRowsPerPass : kRows) * BK;
+  // a stage is padded to whole passes: every lane of a load writes inside it
+  constexpr int kNumBuf = C::NS;
+  constexpr int kBufElems = kPPT * kRowsPerPass * BK;
   __shared__ __attribute__((aligned(16))) uint16_t lds_all[kNumBuf * kBufElems];
   uint16_t(*lds)[kBufElems] = reinterpret_cast<uint16_t(*)[kBufElems]>(lds_all);
 
@@ -380,7 +367,7 @@ __global__ __launch_bounds__(C::NT) void lmhead_bf16_mfma(
   const int voff0 = srow * row_bytes + spiece * 16;
   const int row_stride_bytes = kRowsPerPass * row_bytes;
 
-  u32x4 pre[PF][kPPT];
+  u32x4 pre[1][kPPT];
   // Loads only; nothing waits on them before the LDS write that needs them.
   // Steps past the end are clamped to the last step (their data is unused).
   auto load_step = [&](u32x4 (&dst)[kPPT], int64_t step) {
@@ -429,7 +416,7 @@ __global__ __launch_bounds__(C::NT) void lmhead_bf16_mfma(
     for (int p = 0; p < kPPT; ++p) {
       const int row = srow + p * kRowsPerPass;
       if (kRows % kRowsPerPass == 0 || row < kRows)
-        *reinterpret_cast<u32x4 *>(buf + lds_piece_offset<BK, SWZ>(row, spiece)) =
+        *reinterpret_cast<u32x4 *>(buf + lds_piece_offset<BK>(row, spiece)) =
             (!VEC || k_in) ? src[p] : u32x4(0);
     }
   };
@@ -440,7 +427,7 @@ __global__ __launch_bounds__(C::NT) void lmhead_bf16_mfma(
 #pragma unroll
     for (int j = 0; j < FM; ++j) acc[i][j] = f32x4(0.f);
 
-  bf16x8 fa[PIPE ? 2 : 1][KS][FN], fb[PIPE ? 2 : 1][KS][FM];
+  bf16x8 fa[1][KS][FN], fb[1][KS][FM];
   auto read_frags_set = [&](int set, const uint16_t *cur, int ks0, int ks1) {
 #pragma unroll
     for (int ks = ks0; ks < ks1; ++ks) {
@@ -448,11 +435,11 @@ __global__ __launch_bounds__(C::NT) void lmhead_bf16_mfma(
 #pragma unroll
       for (int i = 0; i < FN; ++i)
         fa[set][ks][i] = *reinterpret_cast<const bf16x8 *>(
-            cur + lds_piece_offset<BK, SWZ>(wn * TN + i * 16 + frag_row, piece));
+            cur + lds_piece_offset<BK>(wn * TN + i * 16 + frag_row, piece));
 #pragma unroll
       for (int j = 0; j < FM; ++j)
         fb[set][ks][j] = *reinterpret_cast<const bf16x8 *>(
-            cur + lds_piece_offset<BK, SWZ>(BN + wm * TM + j * 16 + frag_row, piece));
+            cur + lds_piece_offset<BK>(BN + wm * TM + j * 16 + frag_row, piece));
     }
   };
   auto mfma_set = [&](int set, int ks0, int ks1) {
@@ -468,7 +455,7 @@ __global__ __launch_bounds__(C::NT) void lmhead_bf16_mfma(
   auto read_frags = [&](const uint16_t *cur, int ks0, int ks1) { read_frags_set(0, cur, ks0, ks1); };
   auto mfma_range = [&](int ks0, int ks1) { mfma_set(0, ks0, ks1); };
 
-  if constexpr (PIPE == 2 && VEC) {
+  if constexpr (VEC) {
     constexpr int NS = C::NS;
     constexpr int kRowsPerWaveLoad = 64 / kPieces;  // rows one wave load instruction fills
     static_assert(BN % kRowsPerWaveLoad == 0, "a load instruction must stay inside W or X");
@@ -530,7 +517,7 @@ __global__ __launch_bounds__(C::NT) void lmhead_bf16_mfma(
       for (int p = 0; p < kPPT; ++p) {
         const int row0 = p * kRowsPerPass + wave_u * kRowsPerWaveLoad;  // wave-uniform
         const int row = row0 + lrow;
-        const int piece = lslot ^ lds_swizzle<BK, SWZ>(row);
+        const int piece = lslot ^ lds_swizzle<BK>(row);
         bool in_w;
         if constexpr (BN % kRowsPerPass == 0) in_w = p * kRowsPerPass < BN;
         else in_w = row0 < BN;
@@ -565,100 +552,28 @@ __global__ __launch_bounds__(C::NT) void lmhead_bf16_mfma(
       rd = (rd + 1 == NS) ? 0 : rd + 1;
       wr = (wr + 1 == NS) ? 0 : wr + 1;
     }
-  } else if constexpr (PIPE == 1) {
-    // (PIPE 2 without 16-byte-aligned rows takes the PIPE 0 path below)
-    static_assert(PF <= 2, "the three-buffer pipeline keeps at most two register sets");
-    // prologue: steps 0 and 1 in LDS buffers 0 and 1, step 2 in registers,
-    // step 0's fragments in register set 0
+  } else {
+    // register-staged two-stage pipeline: step 0 in LDS stage 0, step 1 in
+    // registers; the loads of step kt+2 are issued halfway through step kt's
+    // MFMAs
     load_step(pre[0], 0);
     store_step(pre[0], lds[0], 0);
-    load_step(pre[PF - 1], 1);
-    store_step(pre[PF - 1], lds[1], 1);
-    load_step(pre[0], 2);
-    __syncthreads();
-    read_frags_set(0, lds[0], 0, KS);
-    for (int64_t kb = 0; kb < nk; kb += 2) {
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        const int64_t kt = kb + u;
-        if (kt >= nk) break;
-        __syncthreads();
-        // buffer (kt+1)%3 holds step kt+1 (written one step ago); buffer
-        // (kt+2)%3 held step kt-1, whose fragments were read two steps ago
-        read_frags_set(1 - u, lds[(kt + 1) % 3], 0, KS);
-        store_step(pre[PF == 1 ? 0 : u], lds[(kt + 2) % 3], kt + 2);
-        load_step(pre[PF == 1 ? 0 : 1 - u], kt + 3);
-        mfma_set(u, 0, KS);
-        __builtin_amdgcn_sched_group_barrier(0x100, KS * (FN + FM), 0);  // LDS reads
-        __builtin_amdgcn_sched_group_barrier(0x200, kPPT, 0);            // LDS writes
-        __builtin_amdgcn_sched_group_barrier(0x020, kPPT, 0);            // global loads
-        __builtin_amdgcn_sched_group_barrier(0x008, KS * FN * FM, 0);    // MFMAs
-      }
-    }
-  } else {
-  // prologue: step 0 in LDS buffer 0, steps 1 .. max(PF,2)-1 in registers
-  load_step(pre[0], 0);
-  store_step(pre[0], lds[0], 0);
-  if constexpr (PF == 1) {
     load_step(pre[0], 1);
-  } else {
-#pragma unroll
-    for (int j = 1; j < PF; ++j) load_step(pre[j], j);
-  }
-
-  for (int64_t kb = 0; kb < nk; kb += PF) {
-#pragma unroll
-    for (int u = 0; u < PF; ++u) {
-      const int64_t kt = kb + u;
-      if (kt >= nk) break;
+    for (int64_t kt = 0; kt < nk; ++kt) {
       __syncthreads();
       const uint16_t *cur = lds[kt & 1];
-      if constexpr (RS == 0) {
-        read_frags(cur, 0, KS);
-        // step kt+1 sits in register set (kt+1) % PF
-        store_step(pre[(u + 1) % PF], lds[(kt + 1) & 1], kt + 1);
-        if constexpr (PF == 1) {
-          mfma_range(0, KS / 2);
-          load_step(pre[0], kt + 2);
-          mfma_range(KS / 2, KS);
-          __builtin_amdgcn_sched_group_barrier(0x100, KS * (FN + FM), 0);  // LDS reads
-          __builtin_amdgcn_sched_group_barrier(0x200, kPPT, 0);            // LDS writes
-          __builtin_amdgcn_sched_group_barrier(0x008, (KS / 2) * FN * FM, 0);
-          __builtin_amdgcn_sched_group_barrier(0x020, kPPT, 0);            // global loads
-          __builtin_amdgcn_sched_group_barrier(0x008, (KS - KS / 2) * FN * FM, 0);
-        } else {
-          // set kt % PF held step kt, written to LDS one step ago: refill it
-          load_step(pre[u], kt + PF);
-          mfma_range(0, KS);
-          __builtin_amdgcn_sched_group_barrier(0x100, KS * (FN + FM), 0);
-          __builtin_amdgcn_sched_group_barrier(0x200, kPPT, 0);
-          __builtin_amdgcn_sched_group_barrier(0x020, kPPT, 0);
-          __builtin_amdgcn_sched_group_barrier(0x008, KS * FN * FM, 0);
-        }
-      } else {
-        // first half's fragments, LDS writes, first half's MFMAs with the
-        // second half's fragment reads slotted in before their end
-        constexpr int H = KS / 2;
-        constexpr int kMf0 = H * FN * FM;
-        constexpr int kLate = (kMf0 / 4 > 0) ? kMf0 / 4 : 1;  // MFMAs after the late reads
-        read_frags(cur, 0, H);
-        store_step(pre[(u + 1) % PF], lds[(kt + 1) & 1], kt + 1);
-        mfma_range(0, H);
-        read_frags(cur, H, KS);
-        if constexpr (PF == 1) load_step(pre[0], kt + 2);
-        else load_step(pre[u], kt + PF);
-        mfma_range(H, KS);
-        __builtin_amdgcn_sched_group_barrier(0x100, H * (FN + FM), 0);
-        __builtin_amdgcn_sched_group_barrier(0x200, kPPT, 0);
-        __builtin_amdgcn_sched_group_barrier(0x008, kMf0 - kLate, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, (KS - H) * (FN + FM), 0);
-        __builtin_amdgcn_sched_group_barrier(0x008, kLate, 0);
-        __builtin_amdgcn_sched_group_barrier(0x020, kPPT, 0);
-        __builtin_amdgcn_sched_group_barrier(0x008, (KS - H) * FN * FM, 0);
-      }
+      read_frags(cur, 0, KS);
+      store_step(pre[0], lds[(kt + 1) & 1], kt + 1);
+      mfma_range(0, KS / 2);
+      load_step(pre[0], kt + 2);
+      mfma_range(KS / 2, KS);
+      __builtin_amdgcn_sched_group_barrier(0x100, KS * (FN + FM), 0);  // LDS reads
+      __builtin_amdgcn_sched_group_barrier(0x200, kPPT, 0);            // LDS writes
+      __builtin_amdgcn_sched_group_barrier(0x008, (KS / 2) * FN * FM, 0);
+      __builtin_amdgcn_sched_group_barrier(0x020, kPPT, 0);            // global loads
+      __builtin_amdgcn_sched_group_barrier(0x008, (KS - KS / 2) * FN * FM, 0);
     }
   }
-  }  // PIPE == 0
 
   // the clamped loads past the last step may still be landing in LDS
   __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
@@ -688,7 +603,7 @@ __device__ __forceinline__ void xreg_dma_w(const uint16_t *w, int bytes, uint16_
 #pragma unroll
   for (int p = 0; p < kPPT; ++p) {
     const int row0 = p * kRowsPerPass + wave * 8;  // wave-uniform
-    const int piece = lslot ^ lds_swizzle<BK, 0>(row0 + lrow);
+    const int piece = lslot ^ lds_swizzle<BK>(row0 + lrow);
     const bool ok = w_off[p] >= 0 && k0 + piece * 8 < k_i;
     __builtin_amdgcn_raw_ptr_buffer_load_lds(
         rsrc, (__attribute__((address_space(3))) void *)(base + row0 * BK), 16,
@@ -848,7 +763,7 @@ __global__ __launch_bounds__(WV * 64) void lmhead_bf16_xreg(
 #pragma unroll
         for (int i = 0; i < FN; ++i) {
           const bf16x8 wf = *reinterpret_cast<const bf16x8 *>(
-              cur + lds_piece_offset<BK, 0>(i * 16 + frag_row, ks * 4 + frag_grp));
+              cur + lds_piece_offset<BK>(i * 16 + frag_row, ks * 4 + frag_grp));
 #pragma unroll
           for (int j = 0; j < FM; ++j)
             acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf, xr[u][ks][j], acc[i][j], 0,
@@ -1084,22 +999,27 @@ int launch_lmhead(const void *x, int64_t m, int64_t k, const void *w, int64_t n,
   //  - M > 256: the same tile with X in registers (lmhead_bf16_xreg), three
   //    W stages in LDS; tiles ordered in groups of 2 (4 past M = 1024) W
   //    tiles so that an XCD's concurrent tiles share W and X in its L2.
+  // 16-byte loads straight to LDS need K % 8 == 0 and 16-byte-aligned bases
+  const bool direct_ok =
+      k % 8 == 0 && ((reinterpret_cast<uint64_t>(x) | reinterpret_cast<uint64_t>(w)) & 15) == 0;
   int rc;
   if (m <= 16 && (n + 127) / 128 < 512)
     // few vocabulary rows (a long K per row): 64-row tiles double the tiles
     // in flight, 128-wide k steps keep the bytes per stage
-    rc = launch_bf16_cfg<Cfg<64, 16, 4, 1, 128, 1, 0, 0, 2, 6>>(xb, m, k, wb, n, ob, ld, col_offset, st, 1, cu, n_tokens, pick);
+    rc = launch_bf16_cfg<Cfg<64, 16, 4, 1, 128, 6>>(xb, m, k, wb, n, ob, ld, col_offset, st, 1, cu, n_tokens, pick);
   else if (m <= 16)
-    rc = launch_bf16_cfg<Cfg<128, 16, 4, 1, 64, 1, 0, 0, 2, 4>>(xb, m, k, wb, n, ob, ld, col_offset, st, 1, cu, n_tokens, pick);
+    rc = launch_bf16_cfg<Cfg<128, 16, 4, 1, 64, 4>>(xb, m, k, wb, n, ob, ld, col_offset, st, 1, cu, n_tokens, pick);
   else if (m <= 32)
-    rc = launch_bf16_cfg<Cfg<128, 32, 4, 1, 64, 1, 0, 0, 2, 4>>(xb, m, k, wb, n, ob, ld, col_offset, st, 1, cu, n_tokens, pick);
+    rc = launch_bf16_cfg<Cfg<128, 32, 4, 1, 64, 4>>(xb, m, k, wb, n, ob, ld, col_offset, st, 1, cu, n_tokens, pick);
   else if (m <= 64)
-    rc = launch_bf16_cfg<Cfg<128, 64, 4, 1, 64, 1, 0, 0, 2, 4>>(xb, m, k, wb, n, ob, ld, col_offset, st, 1, cu, n_tokens, pick);
-  else if (m <= 128)
-    rc = launch_bf16_cfg<Cfg<256, 128, 4, 2, 64, 1, 0, 0, 2, 3>>(xb, m, k, wb, n, ob, ld, col_offset, st, 4, cu, n_tokens, pick);
+    rc = launch_bf16_cfg<Cfg<128, 64, 4, 1, 64, 4>>(xb, m, k, wb, n, ob, ld, col_offset, st, 1, cu, n_tokens, pick);
+  else if (m <= 128 || !direct_ok)
+    // (operands that cannot take 16-byte loads go through registers; the
+    // 256 x 128 tile keeps that path free of spills)
+    rc = launch_bf16_cfg<Cfg<256, 128, 4, 2, 64, 3>>(xb, m, k, wb, n, ob, ld, col_offset, st, 4, cu, n_tokens, pick);
   else if (m <= 256 || !launch_bf16_xreg<320, 8, 32, 3>(xb, m, k, wb, n, ob, ld, col_offset, st,
                                                        m > 1024 ? 4 : 2, cu, n_tokens, pick, &rc))
-    rc = launch_bf16_cfg<Cfg<320, 256, 2, 4, 64, 1, 0, 0, 2, 2>>(xb, m, k, wb, n, ob, ld, col_offset, st, 1, cu, n_tokens, pick);
+    rc = launch_bf16_cfg<Cfg<320, 256, 2, 4, 64, 2>>(xb, m, k, wb, n, ob, ld, col_offset, st, 1, cu, n_tokens, pick);
   if (rc != 0) return rc;
   return static_cast<int>(hipGetLastError());
 }
