@@ -617,3 +617,55 @@ def test_weight_loader_and_tied_head():
     with pytest.raises(ValueError):
         vpe.ParallelLMHead(V, D, tp_size=tp, tp_rank=0, device=dev()).tie_to(
             vpe.VocabParallelEmbedding(V, D, tp_size=tp, tp_rank=1, device=dev()))
+
+
+# ---------------------------------------------------------------------------
+# the path captured in a HIP graph: replays match eager launches bit for bit
+# ---------------------------------------------------------------------------
+def test_graph_replays_match_eager():
+    V, D, tp, n_ids, m = 4096, 256, 2, 999, 40
+    full = wl.table_rows(800, V, D, "bf16", 0, V)
+    ids_d = to_dev(wl.token_ids(801, V, n_ids))
+    x_d = to_dev(wl.hidden_states(802, m, D, "bf16"))
+    shards = [to_dev(full[r * V // tp:(r + 1) * V // tp]) for r in range(tp)]
+    starts = [r * V // tp for r in range(tp)]
+
+    def path(parts, total, logits, best):
+        for r in range(tp):
+            vpe.vpe_embed(ids_d, shards[r], starts[r], out=parts[r])
+        vpe.vpe_sum_partials(parts, out=total)
+        for r in range(tp):
+            vpe.vpe_lmhead(x_d, shards[r], logits, col_offset=starts[r])
+        vpe.vpe_argmax_init(best)
+        for r in range(tp):
+            vpe.vpe_lmhead_argmax(x_d, shards[r], starts[r], best)
+        return vpe.vpe_argmax_decode(best)
+
+    def buffers():
+        return ([torch.empty((n_ids, D), dtype=torch.bfloat16, device=dev()) for _ in range(tp)],
+                torch.empty((n_ids, D), dtype=torch.bfloat16, device=dev()),
+                torch.empty((m, V), dtype=torch.bfloat16, device=dev()),
+                torch.empty(m, dtype=torch.int64, device=dev()))
+
+    eb = buffers()
+    e_val, e_tok = path(*eb)
+    torch.cuda.synchronize()
+    gb = buffers()
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream(device=dev())
+    with torch.cuda.graph(g, stream=side):
+        g_val, g_tok = path(*gb)
+    for rep in range(3):
+        # eager work between replays, including clearing every output
+        for t in gb[0] + [gb[1], gb[2], gb[3]]:
+            t.zero_()
+        g_val.zero_()
+        g_tok.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for a, b in zip(eb[0] + [eb[1], eb[2]], gb[0] + [gb[1], gb[2]]):
+            assert to_host(a).tobytes() == to_host(b).tobytes(), f"replay {rep}"
+        assert torch.equal(e_tok, g_tok) and torch.equal(e_val, g_val), f"replay {rep}"
+    # and the eager results are right
+    assert to_host(eb[1]).tobytes() == oracle.embed(to_host(ids_d), full, 0).tobytes()
