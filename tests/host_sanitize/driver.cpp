@@ -1,0 +1,171 @@
+// Host-side driver for the sanitized build (AddressSanitizer + UBSan, host
+// code only): every C-ABI entry point's validation, with edge and overflow-
+// prone arguments, against stand-in launchers that record what they receive;
+// and the CPU oracle's loops on small heap buffers, where any out-of-bounds
+// access is reported.  Exits non-zero on the first failed expectation.
+#include <stdint.h>
+#include <stdio.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include <vector>
+
+#include "../../include/vpe.h"
+#include "stub_record.h"
+
+extern "C" {
+int orc_shard_range(int64_t, int32_t, int32_t, int64_t *, int64_t *);
+int orc_mask_shift(const void *, int, int64_t, int64_t, int64_t, uint8_t *, int64_t *);
+int orc_embed(const void *, int, int64_t, const void *, int, int64_t, int64_t, int64_t, void *,
+              int);
+int orc_sum_partials(const void *const *, int32_t, int64_t, int, void *);
+int orc_last_token_select(const void *, int64_t, int64_t, int, const int32_t *, int64_t, void *);
+int orc_lmhead_f64(const void *, int64_t, int64_t, const void *, int64_t, int, double *, int64_t,
+                   int64_t, int);
+int orc_argmax_rows(const double *, int64_t, int64_t, int64_t, double *, int64_t *);
+int orc_load_shard(const void *, int64_t, int64_t, int, int32_t, int32_t, void *);
+}
+
+static int g_fail = 0;
+#define EXPECT(cond)                                                   \
+  do {                                                                 \
+    if (!(cond)) {                                                     \
+      fprintf(stderr, "%s:%d: expectation failed: %s\n", __FILE__, __LINE__, #cond); \
+      g_fail = 1;                                                      \
+    }                                                                  \
+  } while (0)
+
+static void *fake(uintptr_t off = 0) { return reinterpret_cast<void *>(0x100000 + off); }
+
+static void check_abi() {
+  const int64_t kMax = INT64_MAX, kMin = INT64_MIN;
+  int64_t s = -1, e = -1;
+  EXPECT(vpe_shard_range(151936, 2, 1, &s, &e) == VPE_OK && s == 75968 && e == 151936);
+  EXPECT(vpe_shard_range(kMax, 1, 0, &s, &e) == VPE_OK && s == 0 && e == kMax);
+  EXPECT(vpe_shard_range(kMin, 2, 0, &s, &e) == VPE_ERR_SHARD);
+  EXPECT(vpe_shard_range(10, INT32_MAX, 0, &s, &e) == VPE_ERR_SHARD);
+  EXPECT(vpe_shard_range(10, 2, INT32_MIN, &s, &e) == VPE_ERR_SHARD);
+  EXPECT(vpe_shard_range(10, 2, 0, nullptr, &e) == VPE_ERR_NULL);
+
+  // embed: the launcher gets the row size in bytes and the id width code
+  g_last = stub_call{};
+  EXPECT(vpe_embed(fake(), VPE_I64, 7, fake(4096), VPE_BF16, 100, 3, 50, fake(8192), nullptr) ==
+         VPE_OK);
+  EXPECT(!strcmp(g_last.what, "embed") && g_last.n0 == 7 && g_last.n1 == 100 && g_last.n2 == 6 &&
+         g_last.n3 == 50 && g_last.i0 == 1);
+  EXPECT(vpe_embed(fake(), VPE_I32, kMax, fake(), VPE_F32, 1, 1, 0, fake(), nullptr) ==
+         VPE_ERR_SHAPE);
+  EXPECT(vpe_embed(fake(), VPE_I32, 1, fake(), VPE_F32, kMax, kMax, 0, fake(), nullptr) ==
+         VPE_ERR_SHAPE);
+  EXPECT(vpe_embed(fake(), VPE_I32, kMin, fake(), VPE_F32, 1, 1, 0, fake(), nullptr) ==
+         VPE_ERR_SHAPE);
+  EXPECT(vpe_embed(fake(), (vpe_itype)7, 1, fake(), VPE_F32, 1, 1, 0, fake(), nullptr) ==
+         VPE_ERR_DTYPE);
+  EXPECT(vpe_embed(fake(2), VPE_I32, 1, fake(), VPE_F32, 1, 1, 0, fake(), nullptr) ==
+         VPE_ERR_ALIGN);
+
+  // sum: 64 partials accepted, 65 rejected, a null entry rejected
+  std::vector<const void *> parts(65, fake());
+  EXPECT(vpe_sum_partials(parts.data(), 64, 10, VPE_BF16, fake(), nullptr) == VPE_OK);
+  EXPECT(!strcmp(g_last.what, "sum") && g_last.n1 == 64 && g_last.i0 == 1);
+  EXPECT(vpe_sum_partials(parts.data(), 65, 10, VPE_BF16, fake(), nullptr) == VPE_ERR_SHAPE);
+  parts[3] = nullptr;
+  EXPECT(vpe_sum_partials(parts.data(), 8, 10, VPE_BF16, fake(), nullptr) == VPE_ERR_NULL);
+  EXPECT(vpe_sum_partials(parts.data(), 0, 10, VPE_BF16, fake(), nullptr) == VPE_ERR_SHAPE);
+
+  // select
+  EXPECT(vpe_last_token_select(fake(), (int64_t)INT32_MAX + 1, 4, VPE_F32, (const int32_t *)fake(),
+                               1, fake(), nullptr) == VPE_ERR_SHAPE);
+  EXPECT(vpe_last_token_select(fake(), 10, 4, VPE_F32, (const int32_t *)fake(2), 1, fake(),
+                               nullptr) == VPE_ERR_ALIGN);
+  EXPECT(vpe_last_token_select(fake(), 10, 4, VPE_F32, (const int32_t *)fake(), 3, fake(),
+                               nullptr) == VPE_OK);
+  EXPECT(!strcmp(g_last.what, "select") && g_last.n0 == 10 && g_last.n1 == 3 && g_last.n2 == 16);
+
+  // LM head: column window and overflow-prone ranges
+  EXPECT(vpe_lmhead(fake(), 4, 64, fake(), 100, VPE_BF16, fake(), 150, 50, nullptr) == VPE_OK);
+  EXPECT(!strcmp(g_last.what, "lmhead") && g_last.n0 == 4 && g_last.n1 == 100 &&
+         g_last.n2 == 64 && g_last.n3 == 50 && g_last.n4 == 150);
+  EXPECT(vpe_lmhead(fake(), 4, 64, fake(), 100, VPE_BF16, fake(), 150, 51, nullptr) ==
+         VPE_ERR_RANGE);
+  EXPECT(vpe_lmhead(fake(), 4, 64, fake(), 100, VPE_BF16, fake(), kMax, kMax, nullptr) ==
+         VPE_ERR_RANGE);
+  EXPECT(vpe_lmhead(fake(), 4, 64, fake(), 100, VPE_BF16, fake(), kMin, 0, nullptr) ==
+         VPE_ERR_RANGE);
+  EXPECT(vpe_lmhead(fake(), 4, 64, fake(), 100, VPE_BF16, fake(), 150, kMin, nullptr) ==
+         VPE_ERR_RANGE);
+  EXPECT(vpe_lmhead(fake(), 1 << 21, 64, fake(), 100, VPE_BF16, fake(), kMax / 2, 0, nullptr) ==
+         VPE_ERR_SHAPE);
+  EXPECT(vpe_lmhead_prefill(fake(), 100, 64, (const int32_t *)fake(), 9, fake(), 100, VPE_BF16,
+                            fake(), 100, 0, nullptr) == VPE_OK);
+  EXPECT(!strcmp(g_last.what, "lmhead_prefill") && g_last.n0 == 9 && g_last.n4 == 100);
+
+  // greedy pick: the id range must fit the keys' 32-bit id field
+  EXPECT(vpe_lmhead_argmax(fake(), 4, 64, fake(), 100, VPE_BF16, 7, (uint64_t *)fake(), nullptr) ==
+         VPE_OK);
+  EXPECT(!strcmp(g_last.what, "lmhead_argmax") && g_last.n3 == 7);
+  EXPECT(vpe_lmhead_argmax(fake(), 4, 64, fake(), 100, VPE_BF16, kMax, (uint64_t *)fake(),
+                           nullptr) == VPE_ERR_RANGE);
+  EXPECT(vpe_lmhead_argmax(fake(), 4, 64, fake(), 100, VPE_BF16, kMin, (uint64_t *)fake(),
+                           nullptr) == VPE_ERR_RANGE);
+  // ids up to 2^32 - 2 fit (vocab_start + shard_rows <= 2^32 - 1)
+  EXPECT(vpe_lmhead_argmax(fake(), 4, 64, fake(), 100, VPE_BF16, 4294967295LL - 99,
+                           (uint64_t *)fake(), nullptr) == VPE_ERR_RANGE);
+  EXPECT(vpe_lmhead_argmax(fake(), 4, 64, fake(), 100, VPE_BF16, 4294967295LL - 100,
+                           (uint64_t *)fake(), nullptr) == VPE_OK);
+  EXPECT(vpe_argmax_init((uint64_t *)fake(), kMax, nullptr) == VPE_ERR_SHAPE);
+  EXPECT(vpe_argmax_decode((const uint64_t *)fake(), 5, (float *)fake(), nullptr, nullptr) ==
+         VPE_OK);
+
+  // shard loading: the launcher copies the rank's contiguous rows
+  EXPECT(vpe_load_shard(fake(), 100, 8, VPE_BF16, 4, 3, fake(1 << 20), nullptr) == VPE_OK);
+  EXPECT(!strcmp(g_last.what, "copy") && g_last.a == fake(75 * 16) && g_last.n0 == 25 * 16);
+  EXPECT(vpe_load_shard(fake(), kMax, kMax, VPE_BF16, 1, 0, fake(1 << 20), nullptr) ==
+         VPE_ERR_SHAPE);
+  EXPECT(vpe_load_shard(fake(), 100, 8, VPE_BF16, 4, 3, fake(75 * 16 + 8), nullptr) ==
+         VPE_ERR_RANGE);
+
+  for (int c = -1; c <= 9; ++c) EXPECT(vpe_status_string((vpe_status)c) != nullptr);
+}
+
+static void check_oracle() {
+  // a [6, 3] fp32 table, tp 2
+  const int64_t V = 6, D = 3;
+  std::vector<float> table(V * D);
+  for (int64_t i = 0; i < V * D; ++i) table[i] = (float)i;
+  int64_t s = 0, e = 0;
+  EXPECT(orc_shard_range(V, 2, 1, &s, &e) == 0 && s == 3 && e == 6);
+  std::vector<int64_t> ids = {-7, 0, 3, 5, 6, 1 << 30};
+  std::vector<uint8_t> mask(ids.size());
+  std::vector<int64_t> local(ids.size());
+  EXPECT(orc_mask_shift(ids.data(), 1, (int64_t)ids.size(), s, e, mask.data(), local.data()) == 0);
+  std::vector<float> part(ids.size() * D);
+  EXPECT(orc_embed(ids.data(), 1, (int64_t)ids.size(), table.data() + s * D, 0, e - s, D, s,
+                   part.data(), 3) == 0);
+  EXPECT(part[2 * D] == table[3 * D] && part[0] == 0.0f);
+  std::vector<float> other(ids.size() * D, 0.0f), sum(ids.size() * D);
+  const void *pp[2] = {part.data(), other.data()};
+  EXPECT(orc_sum_partials(pp, 2, (int64_t)sum.size(), 0, sum.data()) == 0);
+  std::vector<int32_t> cu = {0, 2, 6};
+  std::vector<float> sel(2 * D);
+  EXPECT(orc_last_token_select(table.data(), V, D, 0, cu.data(), 2, sel.data()) == 0);
+  std::vector<int32_t> bad = {0, 4, 2};
+  EXPECT(orc_last_token_select(table.data(), V, D, 0, bad.data(), 2, sel.data()) != 0);
+  std::vector<double> logits(2 * (V + 1), -1.0);
+  EXPECT(orc_lmhead_f64(sel.data(), 2, D, table.data(), V, 0, logits.data(), V + 1, 1, 4) == 0);
+  std::vector<double> mx(2);
+  std::vector<int64_t> at(2);
+  EXPECT(orc_argmax_rows(logits.data(), 2, V + 1, V + 1, mx.data(), at.data()) == 0);
+  EXPECT(at[0] == 6 && at[1] == 6);  // the last table row has the largest entries
+  std::vector<float> shard((V / 2) * D);
+  EXPECT(orc_load_shard(table.data(), V, D, 0, 2, 1, shard.data()) == 0);
+  EXPECT(shard[0] == table[3 * D]);
+  EXPECT(orc_load_shard(table.data(), V, D, 0, 4, 0, shard.data()) != 0);
+}
+
+int main() {
+  check_abi();
+  check_oracle();
+  if (!g_fail) printf("host sanitizer driver: all expectations held\n");
+  return g_fail;
+}

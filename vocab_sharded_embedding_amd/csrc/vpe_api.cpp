@@ -167,7 +167,8 @@ vpe_status vpe_lmhead_argmax(const void *x, int64_t m, int64_t dim, const void *
   if (m > (int64_t(1) << 21) || dim > (int64_t(1) << 20) || shard_rows > kMaxElems / dim)
     return VPE_ERR_SHAPE;
   // ids travel in 32 bits inside the keys
-  if (vocab_start < 0 || vocab_start + shard_rows > (int64_t(1) << 32) - 1) return VPE_ERR_RANGE;
+  // (compared without forming vocab_start + shard_rows, which may overflow)
+  if (vocab_start < 0 || vocab_start > (int64_t(1) << 32) - 1 - shard_rows) return VPE_ERR_RANGE;
   if (m == 0) return VPE_OK;
   if (!x || !weight || !best) return VPE_ERR_NULL;
   if (!aligned(x, dtype_bytes(dt)) || !aligned(weight, dtype_bytes(dt)) || !aligned(best, 8))
