@@ -669,3 +669,60 @@ def test_graph_replays_match_eager():
         assert torch.equal(e_tok, g_tok) and torch.equal(e_val, g_val), f"replay {rep}"
     # and the eager results are right
     assert to_host(eb[1]).tobytes() == oracle.embed(to_host(ids_d), full, 0).tobytes()
+
+
+# ---------------------------------------------------------------------------
+# seeded random shapes: every kernel variant's edges, many times over
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_random_lmhead_shapes_and_windows(dtype):
+    rng = np.random.default_rng(900 if dtype == "bf16" else 901)
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    for case in range(24):
+        m = int(rng.choice([1, 2, 7, 16, 17, 33, 64, 65, 129, 256, 257, 300, 513]))
+        n = int(rng.integers(1, 1400))
+        k = int(rng.choice([1, 8, 24, 40, 64, 72, 100, 128, 200, 264, 520]))
+        col = int(rng.integers(0, 20)) * (8 if rng.random() < 0.7 else 1)
+        ld = col + n + int(rng.integers(0, 24))
+        X = wl.hidden_states(1000 + case, m, k, dtype)
+        W = wl.table_rows(1100 + case, n, k, dtype, 0, n, std=0.5)
+        logits = torch.full((m, ld), -1536.0, dtype=tdt, device=dev())
+        vpe.vpe_lmhead(to_dev(X), to_dev(W), logits, col_offset=col)
+        got = to_host(logits)
+        what = f"{dtype} case {case}: m={m} n={n} k={k} ld={ld} col={col}"
+        assert_logits_close(got[:, col:col + n], oracle.lmhead_f64(X, W, nthreads=oracle_threads()),
+                            what)
+        g = as_f64(got)
+        assert np.all(g[:, :col] == -1536.0) and np.all(g[:, col + n:] == -1536.0), what
+        if dtype == "bf16":
+            # the greedy pick agrees with the stored logits
+            val, tok = _pick(to_dev(X), [to_dev(W)], [col])
+            assert np.array_equal(tok - col, np.argmax(g[:, col:col + n], axis=1)), what
+            assert np.array_equal(val, g[:, col:col + n].max(axis=1)), what
+
+
+def test_random_prefill_and_lookups():
+    rng = np.random.default_rng(902)
+    for case in range(16):
+        dtype = "bf16" if case % 2 == 0 else "f32"
+        seqs = int(rng.integers(1, 400))
+        dim = int(rng.choice([8, 16, 24, 64, 96, 136]))
+        rows = int(rng.integers(1, 900))
+        cu = wl.cu_seqlens_ragged(1200 + case, seqs, 1, 30)
+        H = wl.hidden_states(1300 + case, int(cu[-1]), dim, dtype)
+        W = wl.table_rows(1400 + case, rows, dim, dtype, 0, rows, std=0.5)
+        what = f"case {case}: {dtype} seqs={seqs} dim={dim} rows={rows}"
+        H_d, cu_d, W_d = to_dev(H), to_dev(cu), to_dev(W)
+        got = to_host(vpe.vpe_lmhead_prefill(H_d, cu_d, W_d))
+        sel = oracle.last_token_select(H, cu)
+        assert_logits_close(got, oracle.lmhead_f64(sel, W, nthreads=oracle_threads()), what)
+        assert to_host(vpe.vpe_last_token_select(H_d, cu_d)).tobytes() == sel.tobytes(), what
+        # lookups over the same table as a vocabulary, ids spilling past both ends
+        vocab_start = int(rng.integers(0, 5000))
+        ids = rng.integers(vocab_start - 50, vocab_start + rows + 50, size=int(rng.integers(1, 3000)))
+        ids = ids.astype(np.int64 if case % 3 == 0 else np.int32)
+        got = to_host(vpe.vpe_embed(to_dev(ids), W_d, vocab_start))
+        assert got.tobytes() == oracle.embed(ids, W, vocab_start).tobytes(), what
+        parts = [got, oracle.embed(ids, W, vocab_start + 1)]
+        tot = to_host(vpe.vpe_sum_partials([to_dev(p) for p in parts]))
+        assert tot.tobytes() == oracle.sum_partials(parts).tobytes(), what
