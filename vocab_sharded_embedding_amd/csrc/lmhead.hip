@@ -10,12 +10,23 @@
 // (vocabulary rows, the same layout the embedding reads).  That is the layout
 // the MFMA operand fragments want, so no transpose is ever made.
 //
-// bf16: matrix-core kernel.  Each 256-thread workgroup owns a BN x BM tile
-// of Z^T (BN vocabulary rows by BM hidden rows); tiles of W and X for a
-// 64-wide slice of K are staged through LDS and consumed by
-// v_mfma_f32_16x16x32_bf16.  W is the MFMA "A" operand (16 vocabulary rows per
-// fragment) and X the "B" operand, so each lane ends up owning 4 consecutive
-// vocabulary columns of one logits row: the epilogue writes 8-byte pieces.
+// bf16: two matrix-core kernels built on v_mfma_f32_16x16x32_bf16.  W is the
+// MFMA "A" operand (16 vocabulary rows per fragment) and X the "B" operand, so
+// each lane owns 4 consecutive vocabulary columns of one logits row.
+//  - lmhead_bf16_mfma: a workgroup (256 or 512 threads) owns a BN x BM tile
+//    of Z^T (BN vocabulary rows by BM hidden rows).  W and X slices of BK
+//    columns of K are staged through a multi-stage LDS ring, filled by
+//    direct buffer-to-LDS loads (or through registers when the operands are
+//    not 16-byte aligned).  Used for every M up to 256, and above that when
+//    the next kernel does not apply.
+//  - lmhead_bf16_xreg: for M > 256.  The workgroup's X rows stay in
+//    registers for the whole K loop and only W streams through LDS, so the
+//    LDS read traffic per MFMA is halved.
+// Epilogues: a full tile is staged through LDS and written as 16-byte rows
+// of logits; a partial tile pairs two lanes' 8-byte fragments into 16-byte
+// stores where the alignment allows, else writes 8-byte or single elements.
+// The greedy-pick variant stores no logits and folds each row's best
+// candidate into a 64-bit key instead.
 // fp32: a plain LDS-tiled FMA kernel (fp32 shards are small test shapes).
 #include <hip/hip_runtime.h>
 #include <stdint.h>

@@ -95,8 +95,8 @@ vpe_status vpe_lmhead(const void *x, int64_t m, int64_t dim, const void *weight,
   if (!known_dtype(dt)) return VPE_ERR_DTYPE;
   if (m < 0 || dim < 1 || shard_rows < 1) return VPE_ERR_SHAPE;
   if (m > kMaxElems / dim || shard_rows > kMaxElems / dim) return VPE_ERR_SHAPE;
-  // the grid's second dimension counts blocks of at least 64 rows of X and
-  // must stay below 65536
+  // the fp32 kernel's grid has one y-block per 64 rows of X, and a grid's y
+  // extent must stay below 65536 (bf16 tile counts are checked at launch)
   if (m > (int64_t(1) << 21)) return VPE_ERR_SHAPE;
   // a tile's rows are addressed with 32-bit byte offsets
   if (dim > (int64_t(1) << 20)) return VPE_ERR_SHAPE;
