@@ -61,6 +61,9 @@ def parse_args():
     p.add_argument("--load-shard", action="store_true",
                    help="time loading every rank's shard of the workload from the full table "
                         "on the device (the weight_loader step) instead of the hot path")
+    p.add_argument("--library-gemm", action="store_true",
+                   help="also time torch.mm (the vendor BLAS) on each LM-head shape, untimed "
+                        "and outside the step, as a reference point for the LM-head kernels")
     p.add_argument("--copy-probe-mib", type=int, default=0,
                    help="after timing, run one device-to-device copy of this many MiB "
                         "(a reference kernel for hardware byte counters)")
@@ -290,6 +293,10 @@ def main():
             run_step(k, bd_evs[k], range(len(kinds)))
         torch.cuda.synchronize()
 
+    lib_gemm = None
+    if args.library_gemm and "lmhead" in kinds:
+        lib_gemm = library_gemm_reference(torch, sets, w, M, args, stream)
+
     if args.copy_probe_mib:
         src = torch.empty(args.copy_probe_mib << 20, dtype=torch.uint8, device=dev)
         dst = torch.empty_like(src)
@@ -297,12 +304,17 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
-    per_kind_ms = {}
+    def pcts(ms):
+        return [round(float(v) * 1e3, 2) for v in np.percentile(ms, [10, 50, 90])]
+
+    per_kind_ms, per_kind_pct = {}, {}
     for j, kind in enumerate(kinds):
         ms = [bd_evs[k][j][0].elapsed_time(bd_evs[k][j][1]) for k in range(n_bd)]
         per_kind_ms.setdefault(kind, []).append(float(np.mean(ms)))
-    dom_ms = [float(np.mean([evs[k][j][0].elapsed_time(evs[k][j][1]) for k in range(args.steps)]))
-              for j in dom_idx]
+        per_kind_pct.setdefault(kind, []).append(pcts(ms))
+    dom_all = [[evs[k][j][0].elapsed_time(evs[k][j][1]) for k in range(args.steps)]
+               for j in dom_idx]
+    dom_ms = [float(np.mean(v)) for v in dom_all]
 
     ms_per_step = t_total * 1e3 / args.steps
     value = step_bytes / (ms_per_step * 1e-3) / 1e9
@@ -313,6 +325,7 @@ def main():
         b = bytes_[kind]
         gbs = [bb / (u * 1e-6) / 1e9 for bb, u in zip(b, us)]
         e = {"us_per_launch": [round(u, 2) for u in us], "launches_per_step": len(us),
+             "us_p10_p50_p90": per_kind_pct[kind],
              "GB_per_s": [round(g, 1) for g in gbs],
              "hbm_frac": [round(g / HBM_PEAK_GBS, 4) for g in gbs]}
         if kind == "embed":
@@ -343,6 +356,7 @@ def main():
                 "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": None,
                 "algorithmic_bytes_per_launch": dom_bytes}
     roof["avg_launch_us"] = round(dom_us, 3)
+    roof["launch_us_p10_p50_p90"] = pcts([v for lst in dom_all for v in lst])
     roof["traffic"] = recorded_traffic(w.name, dom)
     for kind in breakdown:
         breakdown[kind]["hbm_bytes_counted"] = recorded_traffic(w.name, kind)
@@ -367,10 +381,41 @@ def main():
         "roofline": roof,
         "cpu_baseline": cpu,
         "breakdown": breakdown,
+        "library_gemm": lib_gemm,
         "device": torch.cuda.get_device_name(dev),
         "input_gen_s": round(gen_s, 2),
     }
     print(json.dumps(line), flush=True)
+
+
+def library_gemm_reference(torch, sets, w, M, args, stream):
+    """torch.mm (hipBLASLt on ROCm) on each LM-head shape: X [M, D] times a shard's
+    [R, D]^T into a contiguous [M, R] buffer, rotating through the same input copies.
+    A reference point only: the timed step never calls it."""
+    import numpy as np
+    reps = max(1, min(args.steps, 50))
+    out = torch.empty((M, w.shard_rows), dtype=sets[0]["x"].dtype, device=sets[0]["x"].device)
+    res = []
+    with torch.cuda.stream(stream):
+        for r in w.ranks:
+            def launch(k):
+                d = sets[k % len(sets)]
+                torch.mm(d["x"], d["shards"][r].t(), out=out)
+            for k in range(3):
+                launch(k)
+            evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                   for _ in range(reps)]
+            for k in range(reps):
+                evs[k][0].record(stream)
+                launch(k)
+                evs[k][1].record(stream)
+            torch.cuda.synchronize()
+            res.append(float(np.mean([a.elapsed_time(b) for a, b in evs])) * 1e3)
+    flops = 2.0 * M * w.shard_rows * w.dim
+    return {"op": "torch.mm bf16, [M, D] x [R, D]^T -> contiguous [M, R]" if w.dtype == "bf16"
+            else "torch.mm fp32, [M, D] x [R, D]^T -> contiguous [M, R]",
+            "us_per_launch": [round(u, 2) for u in res],
+            "TFLOP_per_s": [round(flops / (u * 1e-6) / 1e12, 2) for u in res]}
 
 
 def bench_load_shard(args, w, lib, dev, up):

@@ -169,6 +169,24 @@ def test_sum_in_place_and_general_values():
     del rng
 
 
+def test_sum_every_part_count():
+    # one to six partials, general (all non-zero) values, sizes spanning
+    # several blocks with ragged vector and element tails; in place as well
+    for dtype in ("f32", "bf16"):
+        epv = 8 if dtype == "bf16" else 4
+        for n_parts in (1, 2, 3, 4, 5, 6):
+            for n in (epv * 512 * 3 + 5 * epv + 3, epv * 1024):
+                parts_h = [wl.hidden_states(60 + 7 * n_parts + r, 1, n, dtype).reshape(-1)
+                           for r in range(n_parts)]
+                parts = [to_dev(p) for p in parts_h]
+                ref = oracle.sum_partials(parts_h)
+                what = (dtype, n_parts, n)
+                assert to_host(vpe.vpe_sum_partials(parts)).tobytes() == ref.tobytes(), what
+                # in place into the last partial
+                vpe.vpe_sum_partials(parts, out=parts[-1])
+                assert to_host(parts[-1]).tobytes() == ref.tobytes(), what
+
+
 # ---------------------------------------------------------------------------
 # last-position select
 # ---------------------------------------------------------------------------

@@ -220,15 +220,15 @@ __device__ __forceinline__ float bf16_bits_to_f32(uint32_t h) { return __uint_as
 // binary32 -> bf16 bits, round to nearest, ties to even; NaN becomes a quiet NaN
 __device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
   const uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
-  return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+  const uint32_t rounded = (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+  return ((u & 0x7fffffffu) > 0x7f800000u) ? ((u >> 16) | 0x40u) : rounded;
 }
 
 // EPV elements per thread: 4 (fp32, 16 B), 8 (bf16, 16 B) or 1 (tail / unaligned)
 template <bool BF16, int EPV>
 __global__ __launch_bounds__(kBlock) void sum_partials_kernel(PartList parts, int n_parts,
                                                              int64_t e0, int64_t n_elems,
-                                                             void *__restrict__ out) {
+                                                             void *out) {
   const int64_t i = e0 + (static_cast<int64_t>(blockIdx.x) * kBlock + threadIdx.x) * EPV;
   if (i >= n_elems) return;
   if constexpr (!BF16) {

@@ -48,8 +48,8 @@ constexpr int kBufferFlags = 0x00020000;
 // binary32 -> bf16 bits, round to nearest, ties to even; NaN becomes a quiet NaN
 __device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
   const uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
-  return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+  const uint32_t rounded = (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+  return ((u & 0x7fffffffu) > 0x7f800000u) ? ((u >> 16) | 0x40u) : rounded;
 }
 
 // ---------------------------------------------------------------------------
