@@ -598,6 +598,21 @@ def test_load_shard_full_vocab_every_rank():
             assert got.tobytes() == oracle.load_shard(full, tp, r).tobytes(), (tp, r)
 
 
+@pytest.mark.parametrize("dtype,dim", [("bf16", 4096), ("bf16", 2056), ("f32", 1030)])
+def test_embed_many_long_rows(dtype, dim):
+    # enough ids for several rows per wave on rows longer than 4 KB, with a
+    # ragged last wave (n % 4 == 3), rows that need two passes of the wave
+    # (2056 bf16 = 257 vectors), 8-byte vectors (1030 fp32), and ids below,
+    # inside and past the shard
+    rng = np.random.default_rng(900 + dim)
+    rows, start, n = 3001, 5000, 4 * 8 * 4 * 256 + 3
+    shard = wl.table_rows(910 + dim, 9000, dim, dtype, start, start + rows)
+    ids = rng.integers(start - 2000, start + rows + 2000, size=n).astype(np.int32)
+    _say(f"embed many long rows {dtype} dim={dim} n={n}")
+    got = to_host(vpe.vpe_embed(to_dev(ids), to_dev(shard), start))
+    assert got.tobytes() == oracle.embed(ids, shard, start, nthreads=oracle_threads()).tobytes()
+
+
 @pytest.mark.parametrize("dtype,vocab,dim", [("f32", 12, 3), ("f32", 96, 5), ("bf16", 30, 7),
                                              ("bf16", 64, 8), ("bf16", 4096, 1000),
                                              ("f32", 6, 1)])

@@ -158,12 +158,16 @@ void launch_gather_chunk(Index index, int64_t n_rows, const V *s, V *d, int64_t 
   } while (0)
     // Several rows per wave put more bytes in flight per wave, but only pay
     // when the grid still has enough waves to fill the chip (8 per SIMD over
-    // 256 CUs); short gathers take one row per wave.
+    // 256 CUs); short gathers take one row per wave.  For 8 KB rows, 4 rows
+    // per wave measured 8% faster than 1 on 131072 ids with a quarter owned
+    // (and 13% faster with none owned, where the wave only stores zeros):
+    // a wave's id loads are paid once for 32 KB of stores.
     const bool many = n_rows >= int64_t(4) * 8 * 4 * 256;
     if (vpl <= 2 && many) VPE_WIDE(2, 4);
     else if (vpl <= 2) VPE_WIDE(2, 1);
     else if (vpl <= 4 && many) VPE_WIDE(4, 2);
     else if (vpl <= 4) VPE_WIDE(4, 1);
+    else if (many) VPE_WIDE(8, 4);
     else VPE_WIDE(8, 1);
 #undef VPE_WIDE
   }

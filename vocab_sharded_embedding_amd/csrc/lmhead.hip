@@ -999,10 +999,14 @@ int launch_lmhead(const void *x, int64_t m, int64_t k, const void *w, int64_t n,
   uint16_t *ob = static_cast<uint16_t *>(logits);
   // Tile shapes by the number of hidden rows M (measured on MI355X):
   //  - M <= 64 (decode-size batches): the LM head streams W once and is
-  //    bound by HBM; narrow tiles of 128 vocabulary rows keep ~1200 tiles
-  //    in flight and four LDS stages keep W loads well ahead of the MFMAs
-  //    (M = 1 over 151936 x 1024 runs at 5.8 TB/s); with fewer than 512
-  //    such tiles (long rows, e.g. 37984 x 4096) 64-row tiles take over;
+  //    bound by HBM, so tiles are narrow and there are many of them, with
+  //    four LDS stages keeping W loads well ahead of the MFMAs.  M <= 16:
+  //    64 vocabulary rows with 128-wide k steps (a sweep over tile heights
+  //    32-192, k steps 64/128 and 3-6 stages found it best or within 2% on
+  //    75968- and 151936-row tables at D = 1024 and on 37984 x 4096).
+  //    M <= 32: 128-row tiles, or 64-row ones when there would be fewer
+  //    than 512 tiles (long rows, e.g. 37984 x 4096: 16% faster); M <= 64:
+  //    128-row tiles;
   //  - 128 < M <= 256: 320 vocabulary rows x 256 hidden rows over 8 waves
   //    (a wave owns 160 x 64), W and X both staged through two LDS stages.
   //    A 75968-row shard is 238 W tiles: one round over 256 CUs, with 0.35
@@ -1015,12 +1019,11 @@ int launch_lmhead(const void *x, int64_t m, int64_t k, const void *w, int64_t n,
   const bool direct_ok =
       k % 8 == 0 && ((reinterpret_cast<uint64_t>(x) | reinterpret_cast<uint64_t>(w)) & 15) == 0;
   int rc;
-  if (m <= 16 && (n + 127) / 128 < 512)
-    // few vocabulary rows (a long K per row): 64-row tiles double the tiles
-    // in flight, 128-wide k steps keep the bytes per stage
-    rc = launch_bf16_cfg<Cfg<64, 16, 4, 1, 128, 6>>(xb, m, k, wb, n, ob, ld, col_offset, st, 1, cu, n_tokens, pick);
-  else if (m <= 16)
-    rc = launch_bf16_cfg<Cfg<128, 16, 4, 1, 64, 4>>(xb, m, k, wb, n, ob, ld, col_offset, st, 1, cu, n_tokens, pick);
+  const bool few_tiles = (n + 127) / 128 < 512;
+  if (m <= 16)
+    rc = launch_bf16_cfg<Cfg<64, 16, 4, 1, 128, 4>>(xb, m, k, wb, n, ob, ld, col_offset, st, 1, cu, n_tokens, pick);
+  else if (m <= 32 && few_tiles)
+    rc = launch_bf16_cfg<Cfg<64, 32, 4, 1, 64, 4>>(xb, m, k, wb, n, ob, ld, col_offset, st, 1, cu, n_tokens, pick);
   else if (m <= 32)
     rc = launch_bf16_cfg<Cfg<128, 32, 4, 1, 64, 4>>(xb, m, k, wb, n, ob, ld, col_offset, st, 1, cu, n_tokens, pick);
   else if (m <= 64)
