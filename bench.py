@@ -16,7 +16,8 @@ table still in the 256 MB Infinity Cache.
 
 Prints ONE JSON line.  The roofline entry is for the dominant kernel (most
 algorithmic bytes): its duration comes from HIP events recorded on the launch
-stream around its launches inside the timed region, the only events there.
+stream around its launches inside the timed region, the only events there
+(timing-only events without the system-scope fence, see TimingEvent).
 The per-kernel breakdown comes from a separate, untimed pass with events
 around every call.
 """
@@ -69,6 +70,69 @@ def parse_args():
                    help="after timing, run one device-to-device copy of this many MiB "
                         "(a reference kernel for hardware byte counters)")
     return p.parse_args()
+
+
+class _Hip:
+    """The HIP runtime this process already uses (the one torch loaded), for
+    timing events that torch's Event does not offer."""
+    lib = None
+
+    @classmethod
+    def get(cls):
+        if cls.lib is None:
+            import ctypes
+            path = None
+            with open("/proc/self/maps") as f:
+                for line in f:
+                    name = line.split()[-1]
+                    if os.path.basename(name).startswith("libamdhip64.so"):
+                        path = name
+                        break
+            if path is None:
+                raise RuntimeError("bench.py: the HIP runtime is not loaded")
+            lib = ctypes.CDLL(path)
+            vp = ctypes.c_void_p
+            lib.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(vp), ctypes.c_uint]
+            lib.hipEventRecord.argtypes = [vp, vp]
+            lib.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), vp, vp]
+            lib.hipEventDestroy.argtypes = [vp]
+            cls.lib = lib
+        return cls.lib
+
+
+class TimingEvent:
+    """A HIP event for timing only, created with hipEventDisableSystemFence: its
+    record is a device timestamp without the system-scope release that a
+    default event performs (an L2 writeback and invalidate that also slows the
+    next kernel).  Elapsed times are read only after a device synchronize, so
+    the event needs no fence to be ordered with the work it brackets."""
+    DISABLE_SYSTEM_FENCE = 0x20000000
+
+    def __init__(self):
+        import ctypes
+        self._hip = _Hip.get()
+        self.ev = ctypes.c_void_p()
+        rc = self._hip.hipEventCreateWithFlags(ctypes.byref(self.ev), self.DISABLE_SYSTEM_FENCE)
+        if rc != 0:
+            raise RuntimeError(f"hipEventCreateWithFlags failed: {rc}")
+
+    def record(self, stream):
+        rc = self._hip.hipEventRecord(self.ev, stream.cuda_stream)
+        if rc != 0:
+            raise RuntimeError(f"hipEventRecord failed: {rc}")
+
+    def elapsed_time(self, end) -> float:
+        """Milliseconds from this event to `end` (both recorded and complete)."""
+        import ctypes
+        ms = ctypes.c_float()
+        rc = self._hip.hipEventElapsedTime(ctypes.byref(ms), self.ev, end.ev)
+        if rc != 0:
+            raise RuntimeError(f"hipEventElapsedTime failed: {rc}")
+        return ms.value
+
+    def __del__(self):
+        if getattr(self, "ev", None) and self.ev.value:
+            self._hip.hipEventDestroy(self.ev)
 
 
 def recorded_traffic(workload: str, kind: str):
@@ -273,7 +337,7 @@ def main():
                 raise RuntimeError(f"{kind} failed: {vpe.status_name(rc)}")
 
     def new_events():
-        return [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+        return [(TimingEvent(), TimingEvent())
                 for _ in kinds]
 
     with torch.cuda.stream(stream):
@@ -406,7 +470,7 @@ def library_gemm_reference(torch, sets, w, M, args, stream):
                 torch.mm(d["x"], d["shards"][r].t(), out=out)
             for k in range(3):
                 launch(k)
-            evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+            evs = [(TimingEvent(), TimingEvent())
                    for _ in range(reps)]
             for k in range(reps):
                 evs[k][0].record(stream)
@@ -461,7 +525,7 @@ def bench_load_shard(args, w, lib, dev, up):
     with torch.cuda.stream(stream):
         for k in range(args.warmup):
             run_step(k)
-        evs = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+        evs = [[(TimingEvent(), TimingEvent())
                 for _ in w.ranks] for _ in range(args.steps)]
         torch.cuda.synchronize()
         t_start = time.perf_counter()
