@@ -598,6 +598,47 @@ def test_load_shard_full_vocab_every_rank():
             assert got.tobytes() == oracle.load_shard(full, tp, r).tobytes(), (tp, r)
 
 
+@pytest.mark.parametrize("dtype,dim,rows", [("bf16", 8, 40), ("bf16", 24, 17), ("f32", 3, 5)])
+def test_lmhead_most_rows(dtype, dim, rows):
+    # the largest M the LM head accepts (2**21 hidden rows): 8192 row tiles of
+    # the large-M kernel, or 32768 row blocks of the fp32 kernel's grid
+    m = 1 << 21
+    x = wl.hidden_states(4300 + dim, m, dim, dtype)
+    w = wl.table_rows(4301 + dim, rows, dim, dtype, 0, rows, std=0.5)
+    _say(f"lmhead most rows: m={m} dim={dim} rows={rows} {dtype}")
+    got = to_host(vpe.vpe_lmhead(to_dev(x), to_dev(w)))
+    assert_logits_close(got, oracle.lmhead_f64(x, w, nthreads=oracle_threads()), "most rows")
+    with pytest.raises(vpe.VpeError):
+        vpe.vpe_lmhead(to_dev(np.zeros((m + 1, dim), dtype=x.dtype)), to_dev(w))
+
+
+def test_embed_past_one_grid():
+    # more rows than one grid takes (2**24 per launch): the lookup is split into
+    # several grids, each starting at its own row of ids and output.  Short rows
+    # (one 4-byte vector) compared in full; rows of 1040 bytes (the multi-row
+    # wave path) sampled around the split and at random, row by row against the
+    # oracle on the same ids.
+    rng = np.random.default_rng(4242)
+    n = (1 << 24) + 1000
+    start, rows = 7000, 50000
+    ids = rng.integers(start - 20000, start + rows + 20000, size=n).astype(np.int32)
+    ids_d = to_dev(ids)
+    shard = wl.table_rows(4243, 80000, 2, "bf16", start, start + rows)
+    _say(f"embed past one grid: n={n} dim=2 bf16")
+    got = to_host(vpe.vpe_embed(ids_d, to_dev(shard), start))
+    assert got.tobytes() == oracle.embed(ids, shard, start, nthreads=oracle_threads()).tobytes()
+    del got
+    shard = wl.table_rows(4244, 80000, 520, "bf16", start, start + rows)
+    _say(f"embed past one grid: n={n} dim=520 bf16")
+    out = vpe.vpe_embed(ids_d, to_dev(shard), start)
+    split = 1 << 24
+    pick = np.concatenate([np.arange(split - 40, split + 40), np.arange(n - 8, n),
+                           rng.integers(0, n, size=2000)])
+    got = to_host(out[torch.from_numpy(pick).to(dev())])
+    del out
+    assert got.tobytes() == oracle.embed(ids[pick], shard, start).tobytes()
+
+
 @pytest.mark.parametrize("dtype,dim", [("bf16", 4096), ("bf16", 2056), ("f32", 1030)])
 def test_embed_many_long_rows(dtype, dim):
     # enough ids for several rows per wave on rows longer than 4 KB, with a
