@@ -512,6 +512,60 @@ def test_argmax_matches_the_stored_logits_bit_for_bit():
         assert np.array_equal(val, stored.max(axis=1))
 
 
+def _first_max_in_key_order(stored_bits):
+    """Per row: (bf16 bits, first column) of the largest 16-bit order code
+    (-0 below +0, a positive NaN above +Inf, a negative one below -Inf)."""
+    h = stored_bits.astype(np.uint32)
+    code = np.where(h & 0x8000, ~h & 0xFFFF, h | 0x8000)
+    col = np.argmax(code, axis=1)
+    return h[np.arange(h.shape[0]), col], col
+
+
+@pytest.mark.parametrize("m", [8, 40, 200, 300])
+@pytest.mark.parametrize("case", ["ties", "inf", "nan", "zero_rows", "tiny"])
+def test_argmax_special_rows_match_stored_logits(m, case):
+    # Rows built so that many distinct fp32 logits round to the same bf16 top
+    # value (the first of them must win), and rows with infinite or NaN logits
+    # or a maximum that rounds to +-0, which the kernels decide on a separate
+    # exact path.  The reference is the first maximum, in key order, of the
+    # logits vpe_lmhead stores for the same inputs.  n = 700 leaves a partial
+    # last tile in every kernel.
+    rng = np.random.default_rng(500 + m)
+    n, k = 700, 32
+    X = np.zeros((m, k), np.float32)
+    W = rng.standard_normal((n, k)).astype(np.float32)
+    X[:, 0] = 1.0
+    X[:, 1] = np.float32(2.0 ** -6)
+    W[:, 0] = rng.integers(0, 4, size=n).astype(np.float32)  # coarse part: many equal tops
+    W[:, 1] = rng.uniform(-1, 1, size=n).astype(np.float32)   # fine part: about one bf16 ulp
+    W[:, 2:] = 0.0
+    Xb, Wb = wl.f32_to_bf16_bits(X), wl.f32_to_bf16_bits(W)
+    if case == "inf":
+        Wb[123, 2] = 0x7F80                     # +Inf: rows with x[2] != 0 see +-Inf, others NaN
+        Xb[::3, 2] = wl.f32_to_bf16_bits(np.float32([[1.0]]))[0, 0]
+    elif case == "nan":
+        Wb[456, 3] = 0x7FC0                     # a NaN column in every row
+    elif case == "zero_rows":
+        Xb[::2, :] = 0                          # +0 rows: every logit is +-0
+        Xb[1::4, :] = 0x8000                    # -0 rows
+    elif case == "tiny":
+        Xb[:, :] = 0
+        Xb[:, 0] = wl.f32_to_bf16_bits(np.float32([[2.0 ** -70]]))[0, 0]
+        Wb[:, 0] = wl.f32_to_bf16_bits(-np.float32(2.0 ** -70) *
+                                       rng.integers(1, 4, size=(n, 1)).astype(np.float32))[:, 0]
+    x_d, w_d = to_dev(Xb), to_dev(Wb)
+    stored = to_host(vpe.vpe_lmhead(x_d, w_d))
+    top, col = _first_max_in_key_order(stored)
+    best = torch.empty(m, dtype=torch.int64, device=dev())
+    vpe.vpe_argmax_init(best)
+    vpe.vpe_lmhead_argmax(x_d, w_d, 5000, best)
+    val, tok = vpe.vpe_argmax_decode(best)
+    tok = to_host(tok)
+    bits = to_host(val).view(np.uint32)
+    assert np.array_equal(tok - 5000, col), f"{case} m={m}"
+    assert np.array_equal(bits >> 16, top) and not np.any(bits & 0xFFFF), f"{case} m={m}"
+
+
 @pytest.mark.parametrize("name", ["qwen3_0p6b_tp2_rank0", "qwen3_0p6b_tp2_all_ranks"])
 def test_argmax_workload_is_a_valid_greedy_pick(name):
     d = _inputs(name)

@@ -129,40 +129,101 @@ constexpr int kBig = 0x7FFF0000;
 // lane's first column and row (nb is a multiple of 4 from a multiple-of-4
 // tile origin).  `full`: the workgroup tile lies wholly inside [0, N) x [0, M).
 // ARGMAX folds each row's largest logit (rounded to bf16) into pick.best.
+template <int FN, int FM>
+__device__ __forceinline__ void argmax_keys(const f32x4 (&acc)[FN][FM], int64_t nb, bool full,
+                                            int64_t N, ArgmaxOut pick, uint64_t (&keys)[FM]) {
+  {
+    // The 4 lanes l, l^16, l^32, l^48 hold the same row m (16 columns each).
+    // Wanted: the row's first largest logit as rounded to bf16, compared in
+    // the key order (16-bit order codes, -0 below +0, NaN outside +-Inf).
+    //
+    // Rounding to nearest even is monotone, so the largest rounded logit is
+    // the rounding `top` of the largest fp32 logit, and the logits that round
+    // to `top` are exactly those at or above the smallest fp32 value that
+    // rounds to it (a bound derived from `top`'s bits).  Fast path: one pass
+    // for the fp32 maximum, one compare per logit for the first column at or
+    // above the bound.  Rows with an infinite or NaN logit, or whose maximum
+    // rounds to +-0 (where fp32 compares do not see the signs of zeros), and
+    // tiles that reach past column N take the exact per-logit path instead.
+#pragma unroll
+    for (int j = 0; j < FM; ++j) {
+      float mx = acc[0][j][0], bad = 0.f;  // bad becomes NaN on an infinite or NaN logit
+#pragma unroll
+      for (int i = 0; i < FN; ++i)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          mx = fmaxf(mx, acc[i][j][r]);
+          bad = fmaf(acc[i][j][r], 0.f, bad);
+        }
+      mx = fmaxf(mx, __shfl_xor(mx, 16));
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      bad = bad + __shfl_xor(bad, 16);
+      bad = bad + __shfl_xor(bad, 32);
+      const uint32_t top = f32_to_bf16_bits(mx);
+      uint64_t key = 0;
+      if (full && bad == 0.f && (top & 0x7FFFu) != 0) {
+        // smallest fp32 rounding to `top`: the midpoint to the next bf16 value
+        // below it, or one ulp past that midpoint when the tie rounds away
+        float lo;
+        if ((top & 0x8000u) == 0) {
+          lo = __uint_as_float((((top - 1u) << 16) | 0x8000u) + (top & 1u));
+        } else {
+          const uint32_t mag = top & 0x7FFFu;  // top = -mag; -Inf: every logit
+          lo = mag >= 0x7F80u ? -__builtin_huge_valf()
+                              : __uint_as_float(0x80000000u | (((mag << 16) | 0x8000u) - (mag & 1u)));
+        }
+        int c = -1;  // this lane's first column at or above lo (columns visited last to first)
+#pragma unroll
+        for (int i = FN - 1; i >= 0; --i)
+#pragma unroll
+          for (int r = 3; r >= 0; --r) c = acc[i][j][r] >= lo ? i * 16 + r : c;
+        if (c >= 0) key = pick_key(__uint_as_float(top << 16), pick.id_base + nb + c);
+      } else {
+        // exact path: visit the columns in increasing order and keep the first
+        // largest 16-bit order code of the rounded logit
+        uint32_t best_ord = 0, best_h = 0;
+        int best_c = -1;  // column offset of the pick inside this lane's columns
+#pragma unroll
+        for (int i = 0; i < FN; ++i)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const uint32_t h = f32_to_bf16_bits(acc[i][j][r]);
+            const uint32_t ord = (h & 0x8000u) ? (~h & 0xFFFFu) : (h | 0x8000u);
+            const bool take = nb + i * 16 + r < N && (best_c < 0 || ord > best_ord);
+            best_ord = take ? ord : best_ord;
+            best_h = take ? h : best_h;
+            best_c = take ? i * 16 + r : best_c;
+          }
+        if (best_c >= 0) key = pick_key(__uint_as_float(best_h << 16), pick.id_base + nb + best_c);
+      }
+      key = umax64(key, __shfl_xor(key, 16));
+      key = umax64(key, __shfl_xor(key, 32));
+      keys[j] = key;
+    }
+  }
+}
+
+// Folds a row's key into pick.best[m] (lanes with (threadIdx.x & 48) == 0
+// hold the keys of rows mb + 16 j).
+template <int FM>
+__device__ __forceinline__ void argmax_fold(const uint64_t (&keys)[FM], int64_t mb, int64_t M,
+                                            ArgmaxOut pick) {
+#pragma unroll
+  for (int j = 0; j < FM; ++j)
+    if ((threadIdx.x & 48) == 0 && mb + j * 16 < M)
+      atomicMax(reinterpret_cast<unsigned long long *>(pick.best + mb + j * 16),
+                static_cast<unsigned long long>(keys[j]));
+}
+
 template <int FN, int FM, bool ARGMAX>
 __device__ __forceinline__ void write_tile(const f32x4 (&acc)[FN][FM], int64_t nb, int64_t mb,
                                            bool full, int64_t M, int64_t N,
                                            uint16_t *__restrict__ out, int64_t ld,
                                            int64_t col_off, ArgmaxOut pick) {
   if constexpr (ARGMAX) {
-    // the 4 lanes l, l^16, l^32, l^48 hold the same row m (16 columns each).
-    // A lane visits its columns in increasing order and keeps the first
-    // largest bf16 logit, comparing 16-bit order codes (the bf16 analogue of
-    // the key's high word); the 64-bit key is built once per row.
-#pragma unroll
-    for (int j = 0; j < FM; ++j) {
-      const int64_t m = mb + j * 16;
-      uint32_t best_ord = 0, best_h = 0;
-      int best_c = -1;  // column offset of the pick inside this lane's columns
-#pragma unroll
-      for (int i = 0; i < FN; ++i)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const uint32_t h = f32_to_bf16_bits(acc[i][j][r]);
-          const uint32_t ord = (h & 0x8000u) ? (~h & 0xFFFFu) : (h | 0x8000u);
-          const bool take = nb + i * 16 + r < N && (best_c < 0 || ord > best_ord);
-          best_ord = take ? ord : best_ord;
-          best_h = take ? h : best_h;
-          best_c = take ? i * 16 + r : best_c;
-        }
-      uint64_t key =
-          best_c < 0 ? 0 : pick_key(__uint_as_float(best_h << 16), pick.id_base + nb + best_c);
-      key = umax64(key, __shfl_xor(key, 16));
-      key = umax64(key, __shfl_xor(key, 32));
-      if ((threadIdx.x & 48) == 0 && m < M)
-        atomicMax(reinterpret_cast<unsigned long long *>(pick.best + m),
-                  static_cast<unsigned long long>(key));
-    }
+    uint64_t keys[FM];
+    argmax_keys<FN, FM>(acc, nb, full, N, pick, keys);
+    argmax_fold<FM>(keys, mb, M, pick);
     return;
   }
   // 8-byte stores need every row start at a multiple of 4 elements from an
@@ -596,6 +657,29 @@ __global__ __launch_bounds__(C::NT) void lmhead_bf16_mfma(
                                     m0 + wm * TM, out, ld, col_off);
       return;
     }
+  }
+  if constexpr (ARGMAX && WN > 1) {
+    // the WN waves that hold the same rows (different columns) combine their
+    // keys in LDS first: one atomic per row per workgroup instead of WN
+    uint64_t keys[FM];
+    argmax_keys<FN, FM>(acc, n0 + wn * TN + 4 * frag_grp, full, N, pick, keys);
+    uint64_t *kl = reinterpret_cast<uint64_t *>(lds_all);  // [WM][FM][16][WN]
+    static_assert(WM * FM * 16 * WN * 8 <= kNumBuf * kBufElems * 2, "key exchange fits the stages");
+    __syncthreads();  // every wave is done with the stages
+    if ((threadIdx.x & 48) == 0) {
+#pragma unroll
+      for (int j = 0; j < FM; ++j) kl[((wm * FM + j) * 16 + frag_row) * WN + wn] = keys[j];
+    }
+    __syncthreads();
+    if (wn == 0) {
+#pragma unroll
+      for (int j = 0; j < FM; ++j)
+#pragma unroll
+        for (int w2 = 1; w2 < WN; ++w2)
+          keys[j] = umax64(keys[j], kl[((wm * FM + j) * 16 + frag_row) * WN + w2]);
+      argmax_fold<FM>(keys, m0 + wm * TM + frag_row, M, pick);
+    }
+    return;
   }
   write_tile<FN, FM, ARGMAX>(acc, n0 + wn * TN + 4 * frag_grp, m0 + wm * TM + frag_row, full, M,
                              N, out, ld, col_off, pick);
