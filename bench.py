@@ -600,7 +600,8 @@ def cpu_baseline(w, ids_h, hidden_h, cu_h, step_bytes, threads):
                                               m_s * w.shard_rows * s for _ in w.ranks)
     return {"value": round(sample_bytes / t / 1e9, 3), "unit": "GB/s", "cores": nt,
             "kind": "oracle",
-            "sample": f"whole step except LM head on {m_s} of {M} rows; {t:.2f} s wall",
+            "sample": f"whole step except LM head on {m_s} of {M} rows; {t:.2f} s wall on "
+                      f"{nt} threads (about {t * nt:.0f} core-seconds)",
             "seconds": round(t, 3)}
 
 
