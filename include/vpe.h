@@ -99,7 +99,8 @@ vpe_status vpe_shard_range(int64_t vocab, int32_t tp_size, int32_t tp_rank,
  * n == 0 is a no-op.  The full (tp = 1) lookup is vocab_start = 0,
  * shard_rows = V.
  * Errors: VPE_ERR_NULL, VPE_ERR_SHAPE (n < 0, dim < 1, shard_rows < 1),
- * VPE_ERR_DTYPE, VPE_ERR_ALIGN (a pointer not aligned to its element size).
+ * VPE_ERR_DTYPE, VPE_ERR_ALIGN (a pointer not aligned to its element size),
+ * VPE_ERR_RANGE (vocab_start < 0, or vocab_start + shard_rows past INT64_MAX).
  */
 vpe_status vpe_embed(const void *ids, vpe_itype itype, int64_t n,
                      const void *weight, vpe_dtype dt, int64_t shard_rows, int64_t dim,

@@ -63,6 +63,14 @@ static void check_abi() {
          VPE_ERR_DTYPE);
   EXPECT(vpe_embed(fake(2), VPE_I32, 1, fake(), VPE_F32, 1, 1, 0, fake(), nullptr) ==
          VPE_ERR_ALIGN);
+  EXPECT(vpe_embed(fake(), VPE_I64, 1, fake(), VPE_F32, 1, 1, -1, fake(), nullptr) ==
+         VPE_ERR_RANGE);
+  EXPECT(vpe_embed(fake(), VPE_I64, 1, fake(), VPE_F32, 1, 1, kMin, fake(), nullptr) ==
+         VPE_ERR_RANGE);
+  EXPECT(vpe_embed(fake(), VPE_I64, 1, fake(), VPE_F32, 100, 1, kMax - 100, fake(), nullptr) ==
+         VPE_OK);
+  EXPECT(vpe_embed(fake(), VPE_I64, 1, fake(), VPE_F32, 100, 1, kMax - 99, fake(), nullptr) ==
+         VPE_ERR_RANGE);
 
   // sum: 64 partials accepted, 65 rejected, a null entry rejected
   std::vector<const void *> parts(65, fake());

@@ -77,6 +77,9 @@ def test_embed_validation():
     assert call(ids=FAKE + 2) == vpe.VPE_ERR_ALIGN
     assert call(itype=I64, ids=FAKE + 4) == vpe.VPE_ERR_ALIGN
     assert call(dt=F32, w=FAKE + 2) == vpe.VPE_ERR_ALIGN
+    assert call(start=-1) == vpe.VPE_ERR_RANGE
+    assert call(start=2 ** 63 - 100) == vpe.VPE_ERR_RANGE
+    assert call(start=2 ** 63 - 101, n=0) == vpe.VPE_OK
     # empty input: valid, enqueues nothing, even with NULL pointers
     assert call(n=0, ids=None, w=None, out=None) == vpe.VPE_OK
 

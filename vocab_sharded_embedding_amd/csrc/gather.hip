@@ -44,10 +44,14 @@ struct ShardIndex {
   const IdT *ids;
   int64_t start;
   int64_t rows;
-  // owned iff start <= id < start + rows; one unsigned compare covers both ends
+  // owned iff start <= id < start + rows; one unsigned compare covers both
+  // ends.  The shift is done modulo 2^64 (no signed overflow for any id); with
+  // 0 <= start <= INT64_MAX - rows (checked on the host) a wrapped difference
+  // is never below rows.
   __device__ __forceinline__ int64_t operator()(int64_t i) const {
-    const int64_t local = static_cast<int64_t>(ids[i]) - start;
-    return (static_cast<uint64_t>(local) < static_cast<uint64_t>(rows)) ? local : -1;
+    const uint64_t local =
+        static_cast<uint64_t>(static_cast<int64_t>(ids[i])) - static_cast<uint64_t>(start);
+    return local < static_cast<uint64_t>(rows) ? static_cast<int64_t>(local) : -1;
   }
   ShardIndex advanced(int64_t r) const { return ShardIndex{ids + r, start, rows}; }
 };

@@ -47,6 +47,8 @@ vpe_status vpe_embed(const void *ids, vpe_itype itype, int64_t n, const void *we
   if (!known_dtype(dt) || !known_itype(itype)) return VPE_ERR_DTYPE;
   if (n < 0 || dim < 1 || shard_rows < 1) return VPE_ERR_SHAPE;
   if (n > kMaxElems / dim || shard_rows > kMaxElems / dim) return VPE_ERR_SHAPE;
+  // the shard's ids [vocab_start, vocab_start + shard_rows) must be representable
+  if (vocab_start < 0 || vocab_start > INT64_MAX - shard_rows) return VPE_ERR_RANGE;
   if (n == 0) return VPE_OK;
   if (!ids || !weight || !out) return VPE_ERR_NULL;
   if (!aligned(ids, itype_bytes(itype)) || !aligned(weight, dtype_bytes(dt)) ||
