@@ -285,7 +285,7 @@ def main():
             seq.append(("sum", lib.vpe_sum_partials,
                         (arr, len(w.ranks), ids_h.size * w.dim, dcode, d["embed_out"].data_ptr(),
                          sh)))
-        fused = bool(w.seqs) and not args.unfused_prefill and not args.argmax
+        fused = bool(w.seqs) and not args.unfused_prefill
         if w.seqs and not fused:
             seq.append(("select", lib.vpe_last_token_select,
                         (d["hidden"].data_ptr(), hidden_h.shape[0], w.dim, dcode,
@@ -293,7 +293,13 @@ def main():
         if args.argmax:
             seq.append(("argmax_init", lib.vpe_argmax_init, (d["best"].data_ptr(), M, sh)))
         for r in w.ranks:
-            if args.argmax:
+            if args.argmax and fused:
+                # the greedy pick reads each sequence's last position itself
+                seq.append(("lmhead_argmax", lib.vpe_lmhead_prefill_argmax,
+                            (d["hidden"].data_ptr(), hidden_h.shape[0], w.dim, d["cu"].data_ptr(),
+                             w.seqs, d["shards"][r].data_ptr(), w.shard_rows, dcode,
+                             w.rank_start(r), d["best"].data_ptr(), sh)))
+            elif args.argmax:
                 seq.append(("lmhead_argmax", lib.vpe_lmhead_argmax,
                             (d["x"].data_ptr(), M, w.dim, d["shards"][r].data_ptr(), w.shard_rows,
                              dcode, w.rank_start(r), d["best"].data_ptr(), sh)))
@@ -315,7 +321,7 @@ def main():
                          d["pick_tok"].data_ptr(), sh)))
         calls.append(seq)
 
-    fused_prefill = bool(w.seqs) and not args.unfused_prefill and not args.argmax
+    fused_prefill = bool(w.seqs) and not args.unfused_prefill
     bytes_, flops_ = algorithmic_bytes(w, ids_h, owned, fused_prefill=fused_prefill,
                                        argmax=args.argmax)
     step_bytes = sum(sum(v) for v in bytes_.values())

@@ -261,6 +261,26 @@ vpe_status vpe_lmhead_argmax(const void *x, int64_t m, int64_t dim, const void *
                              uint64_t *best, void *stream);
 
 /*
+ * vpe_lmhead_argmax over the last position of every packed sequence: the
+ * prefill select folded into the pick as vpe_lmhead_prefill folds it into the
+ * logits ([Guide-3.3] section 6: prefill logits come from each sequence's
+ * last position; [TP-vocab] section 4).  Row s of best takes the largest
+ * logit of hidden[cu_seqlens[s+1]-1] . weight^T with its id.
+ * hidden, n_tokens, dim, cu_seqlens, n_seqs: as vpe_lmhead_prefill (a
+ * sequence whose last index falls outside [0, n_tokens) folds in a row of
+ * zero logits, nothing is read).  weight, shard_rows, dt, vocab_start: as
+ * vpe_lmhead_argmax; best: device uint64 [n_seqs] from vpe_argmax_init.
+ * n_seqs == 0 is a no-op.  The keys equal those of vpe_last_token_select
+ * followed by vpe_lmhead_argmax on the selected rows.
+ * Errors: VPE_ERR_NULL, VPE_ERR_SHAPE (as vpe_lmhead_prefill),
+ * VPE_ERR_RANGE (as vpe_lmhead_argmax), VPE_ERR_DTYPE, VPE_ERR_ALIGN.
+ */
+vpe_status vpe_lmhead_prefill_argmax(const void *hidden, int64_t n_tokens, int64_t dim,
+                                     const int32_t *cu_seqlens, int64_t n_seqs,
+                                     const void *weight, int64_t shard_rows, vpe_dtype dt,
+                                     int64_t vocab_start, uint64_t *best, void *stream);
+
+/*
  * max_logit[i] (device float [m], may be NULL) and token[i] (device int64
  * [m], may be NULL, not both) decoded from best[i], m <= 2^21.  A row no
  * shard folded into decodes to (NaN with the sign bit set, 0xFFFFFFFF).

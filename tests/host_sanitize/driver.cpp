@@ -121,6 +121,20 @@ static void check_abi() {
                            (uint64_t *)fake(), nullptr) == VPE_ERR_RANGE);
   EXPECT(vpe_lmhead_argmax(fake(), 4, 64, fake(), 100, VPE_BF16, 4294967295LL - 100,
                            (uint64_t *)fake(), nullptr) == VPE_OK);
+  // greedy pick over packed sequences: select and pick in one launch
+  EXPECT(vpe_lmhead_prefill_argmax(fake(), 1000, 64, (const int32_t *)fake(), 9, fake(), 100,
+                                   VPE_BF16, 7, (uint64_t *)fake(), nullptr) == VPE_OK);
+  EXPECT(!strcmp(g_last.what, "lmhead_prefill_argmax") && g_last.n0 == 9 && g_last.n3 == 7 &&
+         g_last.n4 == 1000);
+  EXPECT(vpe_lmhead_prefill_argmax(fake(), kMax, 64, (const int32_t *)fake(), 9, fake(), 100,
+                                   VPE_BF16, 7, (uint64_t *)fake(), nullptr) == VPE_ERR_SHAPE);
+  EXPECT(vpe_lmhead_prefill_argmax(fake(), 1000, 64, (const int32_t *)fake(), 9, fake(), kMax,
+                                   VPE_BF16, 7, (uint64_t *)fake(), nullptr) == VPE_ERR_SHAPE);
+  EXPECT(vpe_lmhead_prefill_argmax(fake(), 1000, 64, (const int32_t *)fake(), 9, fake(), 100,
+                                   VPE_BF16, kMin, (uint64_t *)fake(), nullptr) == VPE_ERR_RANGE);
+  EXPECT(vpe_lmhead_prefill_argmax(fake(), 1000, 64, (const int32_t *)fake(), 9, fake(), 100,
+                                   VPE_BF16, 4294967295LL - 99, (uint64_t *)fake(),
+                                   nullptr) == VPE_ERR_RANGE);
   EXPECT(vpe_argmax_init((uint64_t *)fake(), kMax, nullptr) == VPE_ERR_SHAPE);
   EXPECT(vpe_argmax_decode((const uint64_t *)fake(), 5, (float *)fake(), nullptr, nullptr) ==
          VPE_OK);

@@ -31,7 +31,8 @@ int launch_sum_partials(const void *const *parts, int n_parts, int64_t n_elems, 
 int launch_lmhead(const void *x, int64_t m, int64_t k, const void *w, int64_t n, int dtype,
                   void *logits, int64_t ld, int64_t col_offset, void *, const int32_t *cu,
                   int64_t n_tokens, uint64_t *best, int64_t id_base) {
-  g_last = stub_call{best ? "lmhead_argmax" : (cu ? "lmhead_prefill" : "lmhead"),
+  g_last = stub_call{best ? (cu ? "lmhead_prefill_argmax" : "lmhead_argmax")
+                          : (cu ? "lmhead_prefill" : "lmhead"),
                      x, w, best ? static_cast<void *>(best) : logits,
                      m, n, k, best ? id_base : col_offset, dtype, cu ? n_tokens : ld};
   return 0;

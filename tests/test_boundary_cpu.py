@@ -25,7 +25,8 @@ def _declared():
 def test_header_declares_the_calls():
     assert _declared() == sorted(["vpe_shard_range", "vpe_embed", "vpe_sum_partials",
                                   "vpe_last_token_select", "vpe_lmhead", "vpe_lmhead_prefill",
-                                  "vpe_argmax_init", "vpe_lmhead_argmax", "vpe_argmax_decode",
+                                  "vpe_argmax_init", "vpe_lmhead_argmax",
+                                  "vpe_lmhead_prefill_argmax", "vpe_argmax_decode",
                                   "vpe_load_shard", "vpe_status_string"])
 
 
@@ -215,6 +216,35 @@ def test_argmax_validation():
     assert lib.vpe_argmax_init(FAKE, 2 ** 21 + 1, None) == vpe.VPE_ERR_SHAPE
     assert d(FAKE, 2 ** 21 + 1, FAKE, FAKE, None) == vpe.VPE_ERR_SHAPE
     assert f(FAKE, 2 ** 21 + 1, 64, FAKE, 100, BF16, 0, FAKE, None) == vpe.VPE_ERR_SHAPE
+
+
+def test_prefill_argmax_validation():
+    lib = vpe.load_library()
+    f = lib.vpe_lmhead_prefill_argmax
+    ok = dict(h=FAKE, t=1000, d=64, cu=FAKE, s=4, w=FAKE, rows=100, dt=BF16, start=0, best=FAKE)
+
+    def call(**kw):
+        a = {**ok, **kw}
+        return f(a["h"], a["t"], a["d"], a["cu"], a["s"], a["w"], a["rows"], a["dt"], a["start"],
+                 a["best"], None)
+
+    assert call(dt=9) == vpe.VPE_ERR_DTYPE
+    assert call(t=-1) == vpe.VPE_ERR_SHAPE
+    assert call(t=2 ** 31) == vpe.VPE_ERR_SHAPE
+    assert call(s=-1) == vpe.VPE_ERR_SHAPE
+    assert call(s=2 ** 21 + 1) == vpe.VPE_ERR_SHAPE
+    assert call(d=0) == vpe.VPE_ERR_SHAPE
+    assert call(d=2 ** 20 + 8) == vpe.VPE_ERR_SHAPE
+    assert call(rows=0) == vpe.VPE_ERR_SHAPE
+    assert call(start=-1) == vpe.VPE_ERR_RANGE
+    assert call(start=2 ** 32 - 100) == vpe.VPE_ERR_RANGE
+    assert call(h=None) == vpe.VPE_ERR_NULL
+    assert call(cu=None) == vpe.VPE_ERR_NULL
+    assert call(best=None) == vpe.VPE_ERR_NULL
+    assert call(cu=FAKE + 2) == vpe.VPE_ERR_ALIGN
+    assert call(best=FAKE + 4) == vpe.VPE_ERR_ALIGN
+    assert call(dt=F32, w=FAKE + 2) == vpe.VPE_ERR_ALIGN
+    assert call(s=0, h=None, cu=None, w=None, best=None) == vpe.VPE_OK
 
 
 def test_load_shard_validation():

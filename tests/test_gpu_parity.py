@@ -600,6 +600,76 @@ def test_argmax_workload_is_a_valid_greedy_pick(name):
         assert abs(val[m] - at_pick) <= 1e-2 + 1e-2 * abs(at_pick), f"{name} row {m}"
 
 
+def _keys(fn):
+    """Run fn(best) on fresh keys and return the raw keys (uint64 as int64)."""
+    def run(m):
+        best = torch.empty(m, dtype=torch.int64, device=dev())
+        vpe.vpe_argmax_init(best)
+        fn(best)
+        return to_host(best)
+    return run
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("seqs,dim,V,tp", [(1, 64, 100, 1), (7, 200, 999, 3), (37, 1024, 2000, 2),
+                                          (130, 96, 700, 1), (300, 72, 1030, 2)])
+def test_prefill_argmax_equals_select_then_argmax(dtype, seqs, dim, V, tp):
+    # the fused pick reads each sequence's last position itself; its keys must
+    # equal those of the select followed by the pick on the selected rows, for
+    # every shard split, folded in reverse order; one sequence ends past the
+    # tokens (a row of zero logits) and one is empty
+    cu = wl.cu_seqlens_ragged(600 + seqs, seqs, 1, 40).astype(np.int64)
+    if seqs > 2:
+        cu[2] = cu[1]                      # empty sequence 1: its last index is cu[1] - 1
+        cu[-1] = cu[-1] + 5                # last sequence ends past the tokens
+    cu = cu.astype(np.int32)
+    T = int(cu[-2]) + 3 if seqs > 2 else int(cu[-1])
+    H = wl.hidden_states(601 + seqs, T, dim, dtype)
+    full = wl.table_rows(602 + seqs, V, dim, dtype, 0, V, std=0.5)
+    H_d, cu_d = to_dev(H), to_dev(cu)
+    per = V // tp
+    shards = [(r * per, to_dev(full[r * per:(r + 1) * per])) for r in range(tp)]
+    fused = _keys(lambda best: [vpe.vpe_lmhead_prefill_argmax(H_d, cu_d, w, s, best)
+                                for s, w in reversed(shards)])(seqs)
+    X_d = vpe.vpe_last_token_select(H_d, cu_d)
+    unfused = _keys(lambda best: [vpe.vpe_lmhead_argmax(X_d, w, s, best)
+                                  for s, w in reversed(shards)])(seqs)
+    assert np.array_equal(fused, unfused), f"{dtype} S={seqs} D={dim} V={V} tp={tp}"
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_prefill_argmax_exact_on_integer_logits(dtype):
+    # integer hidden states and table: the oracle's first maximum over the
+    # selected rows' exact logits is the unique right answer
+    seqs, dim, V = 45, 64, 1500
+    cu = wl.cu_seqlens_ragged(620, seqs, 1, 30)
+    T = int(cu[-1])
+    rng = np.random.default_rng(621)
+    H = rng.integers(-1, 2, size=(T, dim)).astype(np.float32)
+    W = rng.integers(-1, 2, size=(V, dim)).astype(np.float32)
+    if dtype == "bf16":
+        H, W = wl.f32_to_bf16_bits(H), wl.f32_to_bf16_bits(W)
+    best = torch.empty(seqs, dtype=torch.int64, device=dev())
+    vpe.vpe_argmax_init(best)
+    vpe.vpe_lmhead_prefill_argmax(to_dev(H), to_dev(cu), to_dev(W), 0, best)
+    val, tok = vpe.vpe_argmax_decode(best)
+    ref_max, ref_idx = oracle.argmax_rows(oracle.lmhead_f64(oracle.last_token_select(H, cu), W))
+    assert np.array_equal(to_host(tok), ref_idx)
+    assert np.array_equal(to_host(val).astype(np.float64), ref_max)
+
+
+def test_prefill_argmax_workload():
+    d = _inputs("qwen3_0p6b_tp1_prefill")
+    w = d["w"]
+    _say(f"prefill argmax {w.name}: T={d['hidden'].shape[0]} S={w.seqs} rows={w.shard_rows}")
+    H, cu, Wd = to_dev(d["hidden"]), to_dev(d["cu"]), to_dev(d["shards"][0])
+    fused = _keys(lambda best: vpe.vpe_lmhead_prefill_argmax(H, cu, Wd, 0, best))(w.seqs)
+    stored = as_f64(to_host(vpe.vpe_lmhead_prefill(H, cu, Wd)))
+    val, tok = vpe.vpe_argmax_decode(torch.from_numpy(fused).to(dev()))
+    assert np.array_equal(to_host(tok), np.argmax(stored, axis=1))
+    assert np.array_equal(to_host(val).astype(np.float64), stored.max(axis=1))
+
+
 def test_parallel_lmhead_layer_fold_argmax():
     V, D, tp, m = 1000, 64, 4, 9
     X, full = _int_inputs(390, m, V, D, "bf16")
@@ -612,6 +682,19 @@ def test_parallel_lmhead_layer_fold_argmax():
         head.fold_argmax(to_dev(X), best)
     val, tok = vpe.vpe_argmax_decode(best)
     ref_max, ref_idx = oracle.argmax_rows(oracle.lmhead_f64(X, full))
+    assert np.array_equal(to_host(tok), ref_idx)
+    assert np.array_equal(to_host(val).astype(np.float64), ref_max)
+    # packed sequences: each rank folds in every sequence's last position
+    cu = wl.cu_seqlens_ragged(391, 6, 1, 5)
+    H, _ = _int_inputs(392, int(cu[-1]), 1, D, "bf16")
+    best = torch.empty(6, dtype=torch.int64, device=dev())
+    vpe.vpe_argmax_init(best)
+    for r in range(tp):
+        head = vpe.ParallelLMHead(V, D, tp_size=tp, tp_rank=r, device=dev())
+        head.weight_loader(head.weight, full_d)
+        head.fold_argmax(to_dev(H), best, cu_seqlens=to_dev(cu))
+    val, tok = vpe.vpe_argmax_decode(best)
+    ref_max, ref_idx = oracle.argmax_rows(oracle.lmhead_f64(oracle.last_token_select(H, cu), full))
     assert np.array_equal(to_host(tok), ref_idx)
     assert np.array_equal(to_host(val).astype(np.float64), ref_max)
 

@@ -27,8 +27,8 @@ VPE_MAX_PARTS = 64
 
 EXPORTED_SYMBOLS = ("vpe_shard_range", "vpe_embed", "vpe_sum_partials",
                     "vpe_last_token_select", "vpe_lmhead", "vpe_lmhead_prefill",
-                    "vpe_argmax_init", "vpe_lmhead_argmax", "vpe_argmax_decode",
-                    "vpe_load_shard", "vpe_status_string")
+                    "vpe_argmax_init", "vpe_lmhead_argmax", "vpe_lmhead_prefill_argmax",
+                    "vpe_argmax_decode", "vpe_load_shard", "vpe_status_string")
 
 
 class VpeError(RuntimeError):
@@ -61,6 +61,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.vpe_lmhead_prefill.argtypes = [vp, i64, i64, vp, i64, vp, i64, ci, vp, i64, i64, vp]
     lib.vpe_argmax_init.argtypes = [vp, i64, vp]
     lib.vpe_lmhead_argmax.argtypes = [vp, i64, i64, vp, i64, ci, i64, vp, vp]
+    lib.vpe_lmhead_prefill_argmax.argtypes = [vp, i64, i64, vp, i64, vp, i64, ci, i64, vp, vp]
     lib.vpe_argmax_decode.argtypes = [vp, i64, vp, vp, vp]
     lib.vpe_load_shard.argtypes = [vp, i64, i64, ci, ctypes.c_int32, ctypes.c_int32, vp, vp]
     for name in EXPORTED_SYMBOLS[:-1]:
@@ -313,6 +314,31 @@ def vpe_lmhead_argmax(x, weight, vocab_start: int, best):
     return best
 
 
+def vpe_lmhead_prefill_argmax(hidden, cu_seqlens, weight, vocab_start: int, best):
+    """Fold this shard's greedy pick for the last position of every packed sequence
+    (hidden [T, D], cu_seqlens int32 [S+1]) into best [S], the select folded in."""
+    torch = _torch()
+    _need_device("hidden", hidden)
+    _need_device("cu_seqlens", cu_seqlens)
+    _need_device("weight", weight)
+    _need_device("best", best)
+    if hidden.dim() != 2 or weight.dim() != 2 or hidden.shape[1] != weight.shape[1]:
+        raise ValueError("hidden must be [n_tokens, dim] and weight [shard_rows, dim]")
+    if hidden.dtype != weight.dtype:
+        raise TypeError("hidden and weight must share a dtype")
+    if cu_seqlens.dtype != torch.int32 or cu_seqlens.dim() != 1 or cu_seqlens.numel() < 1:
+        raise ValueError("cu_seqlens must be a 1-D int32 tensor with at least one entry")
+    s = cu_seqlens.numel() - 1
+    if best.dtype != torch.int64 or best.dim() != 1 or best.numel() != s:
+        raise ValueError("best must be an int64 tensor with one key per sequence")
+    _same_device(hidden, cu_seqlens, weight, best)
+    _check("vpe_lmhead_prefill_argmax", load_library().vpe_lmhead_prefill_argmax(
+        hidden.data_ptr(), hidden.shape[0], hidden.shape[1], cu_seqlens.data_ptr(), s,
+        weight.data_ptr(), weight.shape[0], _dtype_code(hidden), int(vocab_start),
+        best.data_ptr(), _stream_handle(hidden.device)))
+    return best
+
+
 def vpe_argmax_decode(best):
     """(max logit float32 [m], token id int64 [m]) from the keys."""
     torch = _torch()
@@ -331,7 +357,7 @@ from .layers import ParallelLMHead, VocabParallelEmbedding  # noqa: E402
 
 __all__ = [
     "vpe_shard_range", "vpe_embed", "vpe_sum_partials", "vpe_last_token_select", "vpe_lmhead",
-    "vpe_lmhead_prefill", "vpe_argmax_init", "vpe_lmhead_argmax", "vpe_argmax_decode",
-    "vpe_load_shard",
+    "vpe_lmhead_prefill", "vpe_argmax_init", "vpe_lmhead_argmax", "vpe_lmhead_prefill_argmax",
+    "vpe_argmax_decode", "vpe_load_shard",
     "VocabParallelEmbedding", "ParallelLMHead", "VpeError", "load_library", "LIB_PATH",
 ]

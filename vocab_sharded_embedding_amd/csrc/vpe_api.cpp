@@ -180,6 +180,27 @@ vpe_status vpe_lmhead_argmax(const void *x, int64_t m, int64_t dim, const void *
                                      vocab_start));
 }
 
+vpe_status vpe_lmhead_prefill_argmax(const void *hidden, int64_t n_tokens, int64_t dim,
+                                     const int32_t *cu_seqlens, int64_t n_seqs,
+                                     const void *weight, int64_t shard_rows, vpe_dtype dt,
+                                     int64_t vocab_start, uint64_t *best, void *stream) {
+  if (!known_dtype(dt)) return VPE_ERR_DTYPE;
+  if (n_tokens < 0 || n_seqs < 0 || dim < 1 || shard_rows < 1) return VPE_ERR_SHAPE;
+  if (n_tokens > INT32_MAX || n_tokens > kMaxElems / dim || shard_rows > kMaxElems / dim)
+    return VPE_ERR_SHAPE;
+  if (n_seqs > (int64_t(1) << 21) || dim > (int64_t(1) << 20)) return VPE_ERR_SHAPE;
+  // ids travel in 32 bits inside the keys (compared without forming the sum)
+  if (vocab_start < 0 || vocab_start > (int64_t(1) << 32) - 1 - shard_rows) return VPE_ERR_RANGE;
+  if (n_seqs == 0) return VPE_OK;
+  if (!hidden || !cu_seqlens || !weight || !best) return VPE_ERR_NULL;
+  if (!aligned(hidden, dtype_bytes(dt)) || !aligned(weight, dtype_bytes(dt)) ||
+      !aligned(cu_seqlens, 4) || !aligned(best, 8))
+    return VPE_ERR_ALIGN;
+  return launched(vpe::launch_lmhead(hidden, n_seqs, dim, weight, shard_rows,
+                                     dt == VPE_BF16 ? 1 : 0, nullptr, shard_rows, 0, stream,
+                                     cu_seqlens, n_tokens, best, vocab_start));
+}
+
 vpe_status vpe_argmax_decode(const uint64_t *best, int64_t m, float *max_logit, int64_t *token,
                              void *stream) {
   if (m < 0 || m > (int64_t(1) << 21)) return VPE_ERR_SHAPE;

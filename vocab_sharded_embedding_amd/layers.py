@@ -17,8 +17,8 @@ from typing import Optional, Sequence
 
 import torch
 
-from . import (vpe_embed, vpe_lmhead, vpe_lmhead_argmax, vpe_lmhead_prefill, vpe_load_shard,
-               vpe_shard_range, vpe_sum_partials)
+from . import (vpe_embed, vpe_lmhead, vpe_lmhead_argmax, vpe_lmhead_prefill,
+               vpe_lmhead_prefill_argmax, vpe_load_shard, vpe_shard_range, vpe_sum_partials)
 
 
 class VocabParallelEmbedding(torch.nn.Module):
@@ -103,7 +103,12 @@ class ParallelLMHead(VocabParallelEmbedding):
             return vpe_lmhead_prefill(hidden, cu_seqlens, self.weight, logits, col_offset=col)
         return vpe_lmhead(hidden, self.weight, logits, col_offset=col)
 
-    def fold_argmax(self, hidden: torch.Tensor, best: torch.Tensor) -> torch.Tensor:
-        """Fold this rank's greedy pick for every row of ``hidden`` into ``best``
-        (keys reset by ``vpe_argmax_init``; read with ``vpe_argmax_decode``)."""
+    def fold_argmax(self, hidden: torch.Tensor, best: torch.Tensor,
+                    cu_seqlens: Optional[torch.Tensor] = None) -> torch.Tensor:
+        """Fold this rank's greedy pick for every row of ``hidden`` (or, with
+        ``cu_seqlens``, for the last position of every packed sequence) into
+        ``best`` (keys reset by ``vpe_argmax_init``; read with ``vpe_argmax_decode``)."""
+        if cu_seqlens is not None:
+            return vpe_lmhead_prefill_argmax(hidden, cu_seqlens, self.weight,
+                                             self.vocab_start_idx, best)
         return vpe_lmhead_argmax(hidden, self.weight, self.vocab_start_idx, best)
