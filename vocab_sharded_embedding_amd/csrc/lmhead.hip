@@ -350,11 +350,12 @@ __device__ __forceinline__ void write_tile_lds(const f32x4 (&acc)[FN][FM], uint1
 //   BK        K slice per pipeline step (64 or 128)
 //   NS        LDS stages (filled by buffer loads that write LDS directly;
 //             NS-1 steps in flight)
+//   NTW       W's loads carry the non-temporal hint.  Decode-size launches
+//             read every W row once (a single tile of hidden rows), and
+//             streaming W that way measured 3-6% faster on MI355X for
+//             M <= 32; where W tiles are shared by several row tiles the
+//             hint is left off.
 // The workgroup has WN * WM waves of 64 lanes.
-// NTW_: W's loads carry the non-temporal hint.  Decode-size launches read
-// every W row exactly once (a single tile of hidden rows), and streaming W
-// that way measured 3-6% faster on MI355X for M <= 32; where W tiles are
-// shared by several row tiles the hint is left off.
 template <int BN_, int BM_, int WN_, int WM_, int BK_, int NS_, bool NTW_ = false>
 struct Cfg {
   static constexpr int BN = BN_, BM = BM_, WN = WN_, WM = WM_, BK = BK_, NS = NS_;
