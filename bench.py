@@ -135,18 +135,29 @@ class TimingEvent:
             self._hip.hipEventDestroy(self.ev)
 
 
+def source_digest(path: str) -> str:
+    """sha256 of a kernel source with its comments and blank space removed: the
+    code the counters were taken with, unchanged by edits to comments alone."""
+    import hashlib
+    import re
+    with open(path) as f:
+        text = f.read()
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    text = re.sub(r"\s+", " ", text).strip()
+    return hashlib.sha256(text.encode()).hexdigest()
+
+
 def recorded_traffic(workload: str, kind: str):
     """HBM bytes per dispatch recorded by hardware counters (profiles/traffic.json),
     or None when none were recorded or the kernel source changed since."""
-    import hashlib
     path = os.path.join(ROOT, "profiles", "traffic.json")
     try:
         with open(path) as f:
             rec = json.load(f)
         k = rec["kernels"][f"{workload}/{kind}"]
-        with open(os.path.join(ROOT, k["source"]), "rb") as f:
-            if hashlib.sha256(f.read()).hexdigest() != k["source_sha256"]:
-                return None
+        if source_digest(os.path.join(ROOT, k["source"])) != k["source_digest"]:
+            return None
         cp = rec["copy_probes"][workload]
         return int((k["fetch_kib"] * cp["fetch_scale"] + k["write_kib"] * cp["write_scale"]) * 1024)
     except (OSError, KeyError, ValueError):
