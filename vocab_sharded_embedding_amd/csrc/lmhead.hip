@@ -46,7 +46,7 @@ constexpr int kBlock = 256;
 constexpr int kBufferFlags = 0x00020000;
 
 // binary32 -> bf16 bits, round to nearest, ties to even; NaN becomes a quiet NaN
-__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
+[[maybe_unused]] __device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
   const uint32_t u = __float_as_uint(f);
   const uint32_t rounded = (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
   return ((u & 0x7fffffffu) > 0x7f800000u) ? ((u >> 16) | 0x40u) : rounded;
@@ -76,7 +76,7 @@ __device__ __forceinline__ uint64_t umax64(uint64_t a, uint64_t b) { return a > 
 
 // Makes v's value needed at this point of the program, so the load that
 // produces it is issued earlier and waited on here, not later.
-__device__ __forceinline__ void pin_vgpr(int32_t &v) { asm volatile("" : "+v"(v)); }
+[[maybe_unused]] __device__ __forceinline__ void pin_vgpr(int32_t &v) { asm volatile("" : "+v"(v)); }
 
 // ---------------------------------------------------------------------------
 // LDS tile layout: a row holds BK bf16 = P = BK/8 pieces of 16 bytes.  The LDS
@@ -106,7 +106,7 @@ __device__ __forceinline__ int lds_piece_offset(int row, int piece) {
 // tiles the inner one.  The ~32 tiles an XCD runs at once then cover GN W
 // tiles times 32/GN X tiles, so both operands are shared in that XCD's L2
 // (GN = 1: all X blocks of one W tile, the order for few X blocks).
-__device__ __forceinline__ void tile_of_block(int b, int tiles_n, int tiles_m, int group_n,
+[[maybe_unused]] __device__ __forceinline__ void tile_of_block(int b, int tiles_n, int tiles_m, int group_n,
                                               int &tn, int &tm) {
   const int total = tiles_n * tiles_m;
   const int xcd = b & 7, idx = b >> 3;
@@ -366,7 +366,7 @@ struct Cfg {
 
 // s_waitcnt immediate that waits until at most n vector-memory operations of
 // this wave are outstanding (LDS and export counters left alone).
-constexpr int vmcnt_imm(int n) { return (n & 0xF) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8); }
+[[maybe_unused]] constexpr int vmcnt_imm(int n) { return (n & 0xF) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8); }
 
 // Z^T tile = W_tile . X_tile^T over K, staged through LDS.  In LDS, rows
 // [0, BN) of a stage hold the W slice and rows [BN, BN+BM) the X slice of a
