@@ -195,7 +195,7 @@ def algorithmic_bytes(w, ids, ranks_owned, fused_prefill=False, argmax=False):
 def main():
     args = parse_args()
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
+        print(f"bench.py: vocab_sharded_embedding_amd runs on one GPU; --gpus {args.gpus} is not supported "
               "(tensor-parallel ranks are emulated on one device)", file=sys.stderr)
         sys.exit(2)
 

@@ -35,7 +35,7 @@ def as_f64(a: np.ndarray) -> np.ndarray:
 
 
 def oracle_threads() -> int:
-    # the GPU machine gives a process a 16-core share whatever the affinity mask says
+    # a GPU host may grant a process a 16-core share whatever its affinity mask says
     return max(1, min(16, len(os.sched_getaffinity(0))))
 
 
