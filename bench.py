@@ -66,6 +66,13 @@ def parse_args():
     p.add_argument("--library-gemm", action="store_true",
                    help="also time torch.mm (the vendor BLAS) on each LM-head shape, untimed "
                         "and outside the step, as a reference point for the LM-head kernels")
+    p.add_argument("--timed-events", choices=("dominant", "none"), default="dominant",
+                   help="HIP events inside the timed region: around each launch of the dominant "
+                        "kernel (default), or none (a diagnostic run for kernel traces of the "
+                        "un-instrumented step; the roofline is then not measured)")
+    p.add_argument("--no-breakdown", action="store_true",
+                   help="skip the separate per-call event pass (a diagnostic run: a kernel "
+                        "trace then holds only the warmup and timed steps)")
     p.add_argument("--copy-probe-mib", type=int, default=0,
                    help="after timing, run one device-to-device copy of this many MiB "
                         "(a reference kernel for hardware byte counters)")
@@ -366,12 +373,13 @@ def main():
         evs = [new_events() for _ in range(args.steps)]
         torch.cuda.synchronize()
         t_start = time.perf_counter()
+        timed_idx = dom_idx if args.timed_events == "dominant" else ()
         for k in range(args.steps):
-            run_step(k, evs[k], dom_idx)
+            run_step(k, evs[k], timed_idx)
         torch.cuda.synchronize()
         t_total = time.perf_counter() - t_start
         # per-kernel breakdown: a separate, untimed pass with every call bracketed
-        n_bd = min(args.steps, 50)
+        n_bd = 0 if args.no_breakdown else min(args.steps, 50)
         bd_evs = [new_events() for _ in range(n_bd)]
         for k in range(n_bd):
             run_step(k, bd_evs[k], range(len(kinds)))
@@ -392,12 +400,12 @@ def main():
         return [round(float(v) * 1e3, 2) for v in np.percentile(ms, [10, 50, 90])]
 
     per_kind_ms, per_kind_pct = {}, {}
-    for j, kind in enumerate(kinds):
+    for j, kind in enumerate(kinds if n_bd else ()):
         ms = [bd_evs[k][j][0].elapsed_time(bd_evs[k][j][1]) for k in range(n_bd)]
         per_kind_ms.setdefault(kind, []).append(float(np.mean(ms)))
         per_kind_pct.setdefault(kind, []).append(pcts(ms))
     dom_all = [[evs[k][j][0].elapsed_time(evs[k][j][1]) for k in range(args.steps)]
-               for j in dom_idx]
+               for j in timed_idx]
     dom_ms = [float(np.mean(v)) for v in dom_all]
 
     ms_per_step = t_total * 1e3 / args.steps
@@ -423,7 +431,7 @@ def main():
         breakdown[kind] = e
 
     # the dominant kernel's duration, from the events of the timed region
-    dom_us = float(np.mean(dom_ms)) * 1e3
+    dom_us = float(np.mean(dom_ms)) * 1e3 if dom_ms else float("nan")
     dom_bytes = float(np.mean(bytes_[dom]))
     dom_flops = float(np.mean(flops_.get(dom, [0])))
     ai = dom_flops / dom_bytes if dom_bytes else 0.0
@@ -440,7 +448,11 @@ def main():
                 "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": None,
                 "algorithmic_bytes_per_launch": dom_bytes}
     roof["avg_launch_us"] = round(dom_us, 3)
-    roof["launch_us_p10_p50_p90"] = pcts([v for lst in dom_all for v in lst])
+    roof["launch_us_p10_p50_p90"] = pcts([v for lst in dom_all for v in lst]) if dom_ms else None
+    if not dom_ms:
+        # no events in the timed region: nothing measured the dominant kernel
+        roof.update(achieved=None, frac=None, avg_launch_us=None,
+                    note="--timed-events none: no events in the timed region")
     roof["traffic"] = recorded_traffic(w.name, dom)
     for kind in breakdown:
         breakdown[kind]["hbm_bytes_counted"] = recorded_traffic(w.name, kind)
