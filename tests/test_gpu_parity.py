@@ -220,6 +220,8 @@ LM_SHAPES = [
     # (m, n, k): tile multiples, ragged tails in every dimension, K not a multiple of 8
     (1, 1, 8), (3, 5, 7), (16, 128, 64), (17, 129, 65), (32, 1000, 200), (64, 777, 1024),
     (65, 300, 96), (128, 256, 128), (130, 515, 264), (257, 131, 40), (300, 2100, 1024),
+    # past 128 rows with K not a multiple of 8: the 256 x 128 tile staged through registers
+    (200, 300, 37), (300, 700, 45),
 ]
 
 
@@ -231,6 +233,32 @@ def test_lmhead_shapes(dtype, m, n, k):
     got = to_host(vpe.vpe_lmhead(to_dev(X), to_dev(W)))
     ref = oracle.lmhead_f64(X, W, nthreads=oracle_threads())
     assert_logits_close(got, ref, f"lmhead {dtype} {m}x{n}x{k}")
+
+
+def _shifted(a, on):
+    """a on the device, one element past a 16-byte boundary when `on` (the
+    boundary requires element alignment only)."""
+    if not on:
+        return to_dev(a)
+    src = to_dev(a)
+    flat = torch.empty(src.numel() + 1, dtype=src.dtype, device=dev())
+    view = flat[1:].view(src.shape)
+    view.copy_(src)
+    assert view.data_ptr() % 16 != 0
+    return view
+
+
+@pytest.mark.parametrize("m", [8, 40, 100, 200, 300])
+@pytest.mark.parametrize("which", ["x", "w", "both"])
+def test_lmhead_unaligned_operands(m, which):
+    # bf16 operands that cannot take 16-byte loads (K a multiple of 8): every
+    # tile shape then stages them through registers
+    n, k = 700, 72
+    X = wl.hidden_states(80 + m, m, k, "bf16")
+    W = wl.table_rows(81, n, k, "bf16", 0, n, std=0.5)
+    x_d, w_d = _shifted(X, which in ("x", "both")), _shifted(W, which in ("w", "both"))
+    got = to_host(vpe.vpe_lmhead(x_d, w_d))
+    assert_logits_close(got, oracle.lmhead_f64(X, W), f"lmhead unaligned {which} m={m}")
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
@@ -464,6 +492,16 @@ def test_argmax_exact_on_integer_logits(dtype, m, n, k):
     ref_max, ref_idx = oracle.argmax_rows(oracle.lmhead_f64(X, W))
     assert np.array_equal(tok, ref_idx), f"{dtype} {m}x{n}x{k}"
     assert np.array_equal(val, ref_max)
+
+
+@pytest.mark.parametrize("m", [8, 100, 300])
+def test_argmax_unaligned_operands(m):
+    # the greedy pick on operands one element past a 16-byte boundary
+    n, k = 900, 64
+    X, W = _int_inputs(400 + m, m, n, k, "bf16")
+    val, tok = _pick(_shifted(X, True), [_shifted(W, True)], [0])
+    ref_max, ref_idx = oracle.argmax_rows(oracle.lmhead_f64(X, W))
+    assert np.array_equal(tok, ref_idx) and np.array_equal(val, ref_max), f"m={m}"
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
