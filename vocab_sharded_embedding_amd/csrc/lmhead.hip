@@ -1100,13 +1100,16 @@ int launch_lmhead(const void *x, int64_t m, int64_t k, const void *w, int64_t n,
   // Tile shapes by the number of hidden rows M (measured on MI355X):
   //  - M <= 64 (decode-size batches): the LM head streams W once and is
   //    bound by HBM, so tiles are narrow and there are many of them, with
-  //    four LDS stages keeping W loads well ahead of the MFMAs.  M <= 16:
+  //    three or four LDS stages keeping W loads well ahead of the MFMAs.
+  //    M <= 16:
   //    64 vocabulary rows with 128-wide k steps (a sweep over tile heights
   //    32-192, k steps 64/128 and 3-6 stages found it best or within 2% on
   //    75968- and 151936-row tables at D = 1024 and on 37984 x 4096).
   //    M <= 32: 128-row tiles, or 64-row ones when there would be fewer
   //    than 512 tiles (long rows, e.g. 37984 x 4096: 16% faster); M <= 64:
-  //    128-row tiles;
+  //    128-row tiles.  The 128-row tiles take three stages, not four: at
+  //    61-74 KB of LDS two workgroups share a CU (M = 64: 6% faster; the
+  //    fused prefill select at M = 32: 3%);
   //  - 128 < M <= 256: 320 vocabulary rows x 256 hidden rows over 8 waves
   //    (a wave owns 160 x 64), W and X both staged through two LDS stages.
   //    A 75968-row shard is 238 W tiles: one round over 256 CUs, with 0.35
@@ -1125,9 +1128,9 @@ int launch_lmhead(const void *x, int64_t m, int64_t k, const void *w, int64_t n,
   else if (m <= 32 && few_tiles)
     rc = launch_bf16_cfg<Cfg<64, 32, 4, 1, 64, 4, true>>(xb, m, k, wb, n, ob, ld, col_offset, st, 1, cu, n_tokens, pick);
   else if (m <= 32)
-    rc = launch_bf16_cfg<Cfg<128, 32, 4, 1, 64, 4, true>>(xb, m, k, wb, n, ob, ld, col_offset, st, 1, cu, n_tokens, pick);
+    rc = launch_bf16_cfg<Cfg<128, 32, 4, 1, 64, 3, true>>(xb, m, k, wb, n, ob, ld, col_offset, st, 1, cu, n_tokens, pick);
   else if (m <= 64)
-    rc = launch_bf16_cfg<Cfg<128, 64, 4, 1, 64, 4, true>>(xb, m, k, wb, n, ob, ld, col_offset, st, 1, cu, n_tokens, pick);
+    rc = launch_bf16_cfg<Cfg<128, 64, 4, 1, 64, 3, true>>(xb, m, k, wb, n, ob, ld, col_offset, st, 1, cu, n_tokens, pick);
   else if (m <= 128 || !direct_ok)
     // (operands that cannot take 16-byte loads go through registers; the
     // 256 x 128 tile keeps that path free of spills)
