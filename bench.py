@@ -293,6 +293,9 @@ def main():
     calls = []  # per copy: list of (kind, fn, args)
     for d in sets:
         seq = []
+        if args.argmax:
+            # the pick's keys are cleared first: anywhere before the first fold will do
+            seq.append(("argmax_init", lib.vpe_argmax_init, (d["best"].data_ptr(), M, sh)))
         for i, r in enumerate(w.ranks):
             seq.append(("embed", lib.vpe_embed,
                         (d["ids"].data_ptr(), icode, ids_h.size, d["shards"][r].data_ptr(), dcode,
@@ -308,8 +311,6 @@ def main():
             seq.append(("select", lib.vpe_last_token_select,
                         (d["hidden"].data_ptr(), hidden_h.shape[0], w.dim, dcode,
                          d["cu"].data_ptr(), w.seqs, d["x"].data_ptr(), sh)))
-        if args.argmax:
-            seq.append(("argmax_init", lib.vpe_argmax_init, (d["best"].data_ptr(), M, sh)))
         for r in w.ranks:
             if args.argmax and fused:
                 # the greedy pick reads each sequence's last position itself
