@@ -187,11 +187,11 @@ def algorithmic_bytes(w, ids, ranks_owned, fused_prefill=False, argmax=False):
     M = w.lm_rows
     R = w.shard_rows
     if argmax:
-        # keys: 8 bytes per row written by the init, folded by every shard,
-        # read by the decode, which writes 4 + 8 bytes per row
-        out["argmax_init"] = [M * 8]
+        # keys: 8 bytes per row folded by every shard, then read and cleared by
+        # the decode (which also writes 4 + 8 bytes per row), so the next step
+        # needs no init
         out["lmhead_argmax"] = [M * D * s + R * D * s + M * 8 for _ in w.ranks]
-        out["argmax_decode"] = [M * (8 + 12)]
+        out["argmax_decode"] = [M * (8 + 8 + 12)]
         flops = {"lmhead_argmax": [2 * M * R * D for _ in w.ranks]}
     else:
         out["lmhead"] = [M * D * s + R * D * s + M * R * s for _ in w.ranks]
@@ -293,9 +293,6 @@ def main():
     calls = []  # per copy: list of (kind, fn, args)
     for d in sets:
         seq = []
-        if args.argmax:
-            # the pick's keys are cleared first: anywhere before the first fold will do
-            seq.append(("argmax_init", lib.vpe_argmax_init, (d["best"].data_ptr(), M, sh)))
         for i, r in enumerate(w.ranks):
             seq.append(("embed", lib.vpe_embed,
                         (d["ids"].data_ptr(), icode, ids_h.size, d["shards"][r].data_ptr(), dcode,
@@ -335,7 +332,8 @@ def main():
                              dcode, d["logits"].data_ptr(), d["logits"].shape[1],
                              w.rank_start(r) if w.concat else 0, sh)))
         if args.argmax:
-            seq.append(("argmax_decode", lib.vpe_argmax_decode,
+            # the decode clears the keys it reads: the next step's folds need no init
+            seq.append(("argmax_decode", lib.vpe_argmax_decode_clear,
                         (d["best"].data_ptr(), M, d["pick_val"].data_ptr(),
                          d["pick_tok"].data_ptr(), sh)))
         calls.append(seq)
@@ -366,6 +364,13 @@ def main():
                 for _ in kinds]
 
     with torch.cuda.stream(stream):
+        if args.argmax:
+            # once per input copy, outside the steps: every step's decode leaves
+            # its copy's keys cleared for that copy's next step
+            for d in sets:
+                rc = lib.vpe_argmax_init(d["best"].data_ptr(), M, sh)
+                if rc != 0:
+                    raise RuntimeError(f"argmax_init failed: {vpe.status_name(rc)}")
         for k in range(args.warmup):
             run_step(k)
         torch.cuda.synchronize()

@@ -236,7 +236,8 @@ vpe_status vpe_load_shard(const void *full, int64_t vocab, int64_t dim, vpe_dtyp
  * Sequence: vpe_argmax_init(best) once; vpe_lmhead_argmax(...) per shard;
  * vpe_argmax_decode(best) -> (max logit, token id) per row.  All on streams
  * ordered by the caller; concurrent shard calls on one `best` are fine (the
- * fold is an atomic max).
+ * fold is an atomic max).  vpe_argmax_decode_clear also resets the keys it
+ * reads, so a decode loop needs vpe_argmax_init only before its first step.
  *
  * The logit compared is the one vpe_lmhead would store: fp32 accumulation
  * rounded to `dt` (round to nearest even), widened back to fp32.
@@ -288,6 +289,15 @@ vpe_status vpe_lmhead_prefill_argmax(const void *hidden, int64_t n_tokens, int64
  */
 vpe_status vpe_argmax_decode(const uint64_t *best, int64_t m, float *max_logit, int64_t *token,
                              void *stream);
+
+/*
+ * vpe_argmax_decode, after which every best[i] is 0 again (each key is
+ * cleared by the thread that read it, in the same kernel), as
+ * vpe_argmax_init would leave it: the next step's folds can follow without
+ * an init call.  Same arguments, outputs and errors as vpe_argmax_decode.
+ */
+vpe_status vpe_argmax_decode_clear(uint64_t *best, int64_t m, float *max_logit,
+                                   int64_t *token, void *stream);
 
 /* Static, NUL-terminated name of a status code ("VPE_OK", ...). */
 const char *vpe_status_string(vpe_status s);

@@ -138,6 +138,11 @@ static void check_abi() {
   EXPECT(vpe_argmax_init((uint64_t *)fake(), kMax, nullptr) == VPE_ERR_SHAPE);
   EXPECT(vpe_argmax_decode((const uint64_t *)fake(), 5, (float *)fake(), nullptr, nullptr) ==
          VPE_OK);
+  EXPECT(vpe_argmax_decode_clear((uint64_t *)fake(), 5, nullptr, (int64_t *)fake(), nullptr) ==
+         VPE_OK);
+  EXPECT(!strcmp(g_last.what, "argmax_decode_clear") && g_last.n0 == 5);
+  EXPECT(vpe_argmax_decode_clear((uint64_t *)fake(), 5, nullptr, nullptr, nullptr) ==
+         VPE_ERR_NULL);
 
   // shard loading: the launcher copies the rank's contiguous rows
   EXPECT(vpe_load_shard(fake(), 100, 8, VPE_BF16, 4, 3, fake(1 << 20), nullptr) == VPE_OK);

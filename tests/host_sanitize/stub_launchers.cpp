@@ -48,6 +48,11 @@ int launch_argmax_decode(const uint64_t *best, int64_t m, float *value, int64_t 
   return 0;
 }
 
+int launch_argmax_decode_clear(uint64_t *best, int64_t m, float *value, int64_t *id, void *) {
+  g_last = stub_call{"argmax_decode_clear", best, value, id, m, 0, 0, 0, 0, 0};
+  return 0;
+}
+
 int launch_copy_bytes(const void *src, void *dst, int64_t n_bytes, void *) {
   g_last = stub_call{"copy", src, nullptr, dst, n_bytes, 0, 0, 0, 0, 0};
   return 0;

@@ -27,6 +27,7 @@ def test_header_declares_the_calls():
                                   "vpe_last_token_select", "vpe_lmhead", "vpe_lmhead_prefill",
                                   "vpe_argmax_init", "vpe_lmhead_argmax",
                                   "vpe_lmhead_prefill_argmax", "vpe_argmax_decode",
+                                  "vpe_argmax_decode_clear",
                                   "vpe_load_shard", "vpe_status_string"])
 
 
@@ -215,6 +216,14 @@ def test_argmax_validation():
     assert d(None, 0, None, None, None) == vpe.VPE_OK
     assert lib.vpe_argmax_init(FAKE, 2 ** 21 + 1, None) == vpe.VPE_ERR_SHAPE
     assert d(FAKE, 2 ** 21 + 1, FAKE, FAKE, None) == vpe.VPE_ERR_SHAPE
+    c = lib.vpe_argmax_decode_clear
+    assert c(FAKE, 4, None, None, None) == vpe.VPE_ERR_NULL
+    assert c(None, 4, FAKE, FAKE, None) == vpe.VPE_ERR_NULL
+    assert c(FAKE, -1, FAKE, FAKE, None) == vpe.VPE_ERR_SHAPE
+    assert c(FAKE, 2 ** 21 + 1, FAKE, FAKE, None) == vpe.VPE_ERR_SHAPE
+    assert c(FAKE + 4, 4, FAKE, FAKE, None) == vpe.VPE_ERR_ALIGN
+    assert c(FAKE, 4, FAKE + 2, FAKE, None) == vpe.VPE_ERR_ALIGN
+    assert c(None, 0, None, None, None) == vpe.VPE_OK
     assert f(FAKE, 2 ** 21 + 1, 64, FAKE, 100, BF16, 0, FAKE, None) == vpe.VPE_ERR_SHAPE
 
 

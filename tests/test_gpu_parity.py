@@ -494,6 +494,31 @@ def test_argmax_exact_on_integer_logits(dtype, m, n, k):
     assert np.array_equal(val, ref_max)
 
 
+@pytest.mark.parametrize("m", [1, 300, 5000])
+def test_argmax_decode_clear_leaves_keys_ready(m):
+    # the clearing decode returns what the plain decode returns and leaves
+    # every key at 0, so a second round of folds needs no init
+    n, k = 700, 64
+    X1, W = _int_inputs(500 + m, m, n, k, "bf16")
+    X2, _ = _int_inputs(600 + m, m, n, k, "bf16")
+    w_d = to_dev(W)
+    best = torch.empty(m, dtype=torch.int64, device=dev())
+    vpe.vpe_argmax_init(best)
+    vpe.vpe_lmhead_argmax(to_dev(X1), w_d, 0, best)
+    keys = best.clone()
+    val1, tok1 = vpe.vpe_argmax_decode_clear(best)
+    val0, tok0 = vpe.vpe_argmax_decode(keys)
+    assert np.array_equal(to_host(tok1), to_host(tok0))
+    assert to_host(val1).tobytes() == to_host(val0).tobytes()
+    assert int(torch.count_nonzero(best)) == 0
+    vpe.vpe_lmhead_argmax(to_dev(X2), w_d, 0, best)
+    val2, tok2 = vpe.vpe_argmax_decode_clear(best)
+    ref_max, ref_idx = oracle.argmax_rows(oracle.lmhead_f64(X2, W))
+    assert np.array_equal(to_host(tok2), ref_idx)
+    assert np.array_equal(to_host(val2).astype(np.float64), ref_max)
+    assert int(torch.count_nonzero(best)) == 0
+
+
 @pytest.mark.parametrize("m", [8, 100, 300])
 def test_argmax_unaligned_operands(m):
     # the greedy pick on operands one element past a 16-byte boundary

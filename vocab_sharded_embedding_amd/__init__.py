@@ -28,7 +28,8 @@ VPE_MAX_PARTS = 64
 EXPORTED_SYMBOLS = ("vpe_shard_range", "vpe_embed", "vpe_sum_partials",
                     "vpe_last_token_select", "vpe_lmhead", "vpe_lmhead_prefill",
                     "vpe_argmax_init", "vpe_lmhead_argmax", "vpe_lmhead_prefill_argmax",
-                    "vpe_argmax_decode", "vpe_load_shard", "vpe_status_string")
+                    "vpe_argmax_decode", "vpe_argmax_decode_clear", "vpe_load_shard",
+                    "vpe_status_string")
 
 
 class VpeError(RuntimeError):
@@ -63,6 +64,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.vpe_lmhead_argmax.argtypes = [vp, i64, i64, vp, i64, ci, i64, vp, vp]
     lib.vpe_lmhead_prefill_argmax.argtypes = [vp, i64, i64, vp, i64, vp, i64, ci, i64, vp, vp]
     lib.vpe_argmax_decode.argtypes = [vp, i64, vp, vp, vp]
+    lib.vpe_argmax_decode_clear.argtypes = [vp, i64, vp, vp, vp]
     lib.vpe_load_shard.argtypes = [vp, i64, i64, ci, ctypes.c_int32, ctypes.c_int32, vp, vp]
     for name in EXPORTED_SYMBOLS[:-1]:
         getattr(lib, name).restype = ci
@@ -339,18 +341,27 @@ def vpe_lmhead_prefill_argmax(hidden, cu_seqlens, weight, vocab_start: int, best
     return best
 
 
-def vpe_argmax_decode(best):
-    """(max logit float32 [m], token id int64 [m]) from the keys."""
+def _decode(name, best):
     torch = _torch()
     _need_device("best", best)
     if best.dtype != torch.int64 or best.dim() != 1:
         raise ValueError("best must be a 1-D int64 tensor (uint64 keys)")
     value = torch.empty(best.shape, dtype=torch.float32, device=best.device)
     token = torch.empty(best.shape, dtype=torch.int64, device=best.device)
-    _check("vpe_argmax_decode", load_library().vpe_argmax_decode(
+    _check(name, getattr(load_library(), name)(
         best.data_ptr(), best.numel(), value.data_ptr(), token.data_ptr(),
         _stream_handle(best.device)))
     return value, token
+
+
+def vpe_argmax_decode(best):
+    """(max logit float32 [m], token id int64 [m]) from the keys."""
+    return _decode("vpe_argmax_decode", best)
+
+
+def vpe_argmax_decode_clear(best):
+    """vpe_argmax_decode, then every key of best is 0 again (ready for the next folds)."""
+    return _decode("vpe_argmax_decode_clear", best)
 
 
 from .layers import ParallelLMHead, VocabParallelEmbedding  # noqa: E402
@@ -358,6 +369,6 @@ from .layers import ParallelLMHead, VocabParallelEmbedding  # noqa: E402
 __all__ = [
     "vpe_shard_range", "vpe_embed", "vpe_sum_partials", "vpe_last_token_select", "vpe_lmhead",
     "vpe_lmhead_prefill", "vpe_argmax_init", "vpe_lmhead_argmax", "vpe_lmhead_prefill_argmax",
-    "vpe_argmax_decode", "vpe_load_shard",
+    "vpe_argmax_decode", "vpe_argmax_decode_clear", "vpe_load_shard",
     "VocabParallelEmbedding", "ParallelLMHead", "VpeError", "load_library", "LIB_PATH",
 ]

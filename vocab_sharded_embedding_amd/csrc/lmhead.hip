@@ -995,7 +995,10 @@ __global__ __launch_bounds__(kBlock) void argmax_init_kernel(uint64_t *__restric
 }
 
 // key -> (logit, id): the inverse of pick_key
-__global__ __launch_bounds__(kBlock) void argmax_decode_kernel(const uint64_t *__restrict__ best,
+// CLEAR: each key is also reset to 0 once read (by the thread that read it),
+// which leaves best ready for the next fold without a separate init.
+template <bool CLEAR>
+__global__ __launch_bounds__(kBlock) void argmax_decode_kernel(uint64_t *__restrict__ best,
                                                               int64_t m, float *__restrict__ value,
                                                               int64_t *__restrict__ id) {
   const int64_t i = static_cast<int64_t>(blockIdx.x) * kBlock + threadIdx.x;
@@ -1005,6 +1008,7 @@ __global__ __launch_bounds__(kBlock) void argmax_decode_kernel(const uint64_t *_
   const uint32_t u = (ord & 0x80000000u) ? (ord & 0x7FFFFFFFu) : ~ord;
   if (value != nullptr) value[i] = __uint_as_float(u);
   if (id != nullptr) id[i] = static_cast<int64_t>(0xFFFFFFFFu - static_cast<uint32_t>(key));
+  if constexpr (CLEAR) best[i] = 0;
 }
 
 template <class C>
@@ -1158,7 +1162,17 @@ int launch_argmax_decode(const uint64_t *best, int64_t m, float *value, int64_t 
                          void *stream) {
   (void)hipGetLastError();
   const dim3 grid(static_cast<unsigned>((m + kBlock - 1) / kBlock));
-  hipLaunchKernelGGL(argmax_decode_kernel, grid, dim3(kBlock), 0,
+  // (the non-clearing kernel only reads best)
+  hipLaunchKernelGGL(argmax_decode_kernel<false>, grid, dim3(kBlock), 0,
+                     static_cast<hipStream_t>(stream), const_cast<uint64_t *>(best), m, value, id);
+  return static_cast<int>(hipGetLastError());
+}
+
+int launch_argmax_decode_clear(uint64_t *best, int64_t m, float *value, int64_t *id,
+                               void *stream) {
+  (void)hipGetLastError();
+  const dim3 grid(static_cast<unsigned>((m + kBlock - 1) / kBlock));
+  hipLaunchKernelGGL(argmax_decode_kernel<true>, grid, dim3(kBlock), 0,
                      static_cast<hipStream_t>(stream), best, m, value, id);
   return static_cast<int>(hipGetLastError());
 }

@@ -211,6 +211,16 @@ vpe_status vpe_argmax_decode(const uint64_t *best, int64_t m, float *max_logit, 
   return launched(vpe::launch_argmax_decode(best, m, max_logit, token, stream));
 }
 
+vpe_status vpe_argmax_decode_clear(uint64_t *best, int64_t m, float *max_logit, int64_t *token,
+                                   void *stream) {
+  if (m < 0 || m > (int64_t(1) << 21)) return VPE_ERR_SHAPE;
+  if (m == 0) return VPE_OK;
+  if (!best || (!max_logit && !token)) return VPE_ERR_NULL;
+  if (!aligned(best, 8) || (max_logit && !aligned(max_logit, 4)) || (token && !aligned(token, 8)))
+    return VPE_ERR_ALIGN;
+  return launched(vpe::launch_argmax_decode_clear(best, m, max_logit, token, stream));
+}
+
 const char *vpe_status_string(vpe_status s) {
   switch (s) {
     case VPE_OK: return "VPE_OK";

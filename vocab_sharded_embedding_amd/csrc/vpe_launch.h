@@ -47,6 +47,10 @@ int launch_argmax_init(uint64_t *best, int64_t m, void *stream);
 int launch_argmax_decode(const uint64_t *best, int64_t m, float *value, int64_t *id,
                          void *stream);
 
+// As launch_argmax_decode, then best[i] = 0.
+int launch_argmax_decode_clear(uint64_t *best, int64_t m, float *value, int64_t *id,
+                               void *stream);
+
 }  // namespace vpe
 
 #endif

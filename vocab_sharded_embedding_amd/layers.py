@@ -107,7 +107,8 @@ class ParallelLMHead(VocabParallelEmbedding):
                     cu_seqlens: Optional[torch.Tensor] = None) -> torch.Tensor:
         """Fold this rank's greedy pick for every row of ``hidden`` (or, with
         ``cu_seqlens``, for the last position of every packed sequence) into
-        ``best`` (keys reset by ``vpe_argmax_init``; read with ``vpe_argmax_decode``)."""
+        ``best`` (keys reset by ``vpe_argmax_init``, or left cleared by
+        ``vpe_argmax_decode_clear``; read with either decode)."""
         if cu_seqlens is not None:
             return vpe_lmhead_prefill_argmax(hidden, cu_seqlens, self.weight,
                                              self.vocab_start_idx, best)
