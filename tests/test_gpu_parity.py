@@ -261,6 +261,18 @@ def test_lmhead_unaligned_operands(m, which):
     assert_logits_close(got, oracle.lmhead_f64(X, W), f"lmhead unaligned {which} m={m}")
 
 
+@pytest.mark.parametrize("m", [8, 24, 40])
+def test_lmhead_unaligned_long_shard(m):
+    # a 70000-row shard takes the 192-row decode tiles; unaligned operands
+    # stage them through registers
+    n, k = 70000, 72
+    X = wl.hidden_states(90 + m, m, k, "bf16")
+    W = wl.table_rows(91, n, k, "bf16", 0, n, std=0.5)
+    got = to_host(vpe.vpe_lmhead(_shifted(X, True), _shifted(W, True)))
+    assert_logits_close(got, oracle.lmhead_f64(X, W, nthreads=oracle_threads()),
+                        f"lmhead unaligned long shard m={m}")
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 @pytest.mark.parametrize("ld,col", [(1500, 0), (1500, 500), (1501, 3), (1003, 1)])
 def test_lmhead_writes_only_its_columns(dtype, ld, col):
@@ -768,6 +780,16 @@ def test_parallel_lmhead_layer_fold_argmax():
 @pytest.mark.parametrize("m", [1, 2, 5, 8, 16])
 @pytest.mark.parametrize("name", ["qwen3_0p6b_tp1_prefill", "large_v151936_d4096_tp4_rank2"])
 def test_lmhead_decode_rows(name, m):
+    _decode_rows(name, m)
+
+
+@pytest.mark.parametrize("m", [1, 5, 16, 24, 32, 48, 64])
+def test_lmhead_decode_rows_tp2_shard(m):
+    # the 75968-row shard takes 192-row decode tiles (one round over the CUs)
+    _decode_rows("qwen3_0p6b_tp2_rank0", m)
+
+
+def _decode_rows(name, m):
     d = _inputs(name)
     w = d["w"]
     W = d["shards"][w.ranks[0]]

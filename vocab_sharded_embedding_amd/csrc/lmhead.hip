@@ -1113,7 +1113,10 @@ int launch_lmhead(const void *x, int64_t m, int64_t k, const void *w, int64_t n,
   //    than 512 tiles (long rows, e.g. 37984 x 4096: 16% faster); M <= 64:
   //    128-row tiles.  The 128-row tiles take three stages, not four: at
   //    61-74 KB of LDS two workgroups share a CU (M = 64: 6% faster; the
-  //    fused prefill select at M = 32: 3%);
+  //    fused prefill select at M = 32: 3%).  Where 192-row tiles fit one
+  //    round at two workgroups per CU (a 75968 x 1024 shard), they replace
+  //    the 64- and 128-row ones: 4-10% faster for M = 16-64 there, within
+  //    1% at M = 1 and 8 (and slower on the full table, where they do not);
   //  - 128 < M <= 256: 320 vocabulary rows x 256 hidden rows over 8 waves
   //    (a wave owns 160 x 64), W and X both staged through two LDS stages.
   //    A 75968-row shard is 238 W tiles: one round over 256 CUs, with 0.35
@@ -1127,12 +1130,22 @@ int launch_lmhead(const void *x, int64_t m, int64_t k, const void *w, int64_t n,
       k % 8 == 0 && ((reinterpret_cast<uint64_t>(x) | reinterpret_cast<uint64_t>(w)) & 15) == 0;
   int rc;
   const bool few_tiles = (n + 127) / 128 < 512;
-  if (m <= 16)
+  // 192-row decode tiles (two LDS stages, two workgroups per CU) when they
+  // fit one round over the 256 CUs at two per CU, e.g. a 75968-row shard
+  // (396 tiles, where 128-row tiles spill 82 tiles into a second round)
+  const bool one_round_192 = !few_tiles && (n + 191) / 192 <= 2 * 256;
+  if (m <= 16 && one_round_192)
+    rc = launch_bf16_cfg<Cfg<192, 16, 4, 1, 64, 2, true>>(xb, m, k, wb, n, ob, ld, col_offset, st, 1, cu, n_tokens, pick);
+  else if (m <= 16)
     rc = launch_bf16_cfg<Cfg<64, 16, 4, 1, 128, 4, true>>(xb, m, k, wb, n, ob, ld, col_offset, st, 1, cu, n_tokens, pick);
   else if (m <= 32 && few_tiles)
     rc = launch_bf16_cfg<Cfg<64, 32, 4, 1, 64, 4, true>>(xb, m, k, wb, n, ob, ld, col_offset, st, 1, cu, n_tokens, pick);
+  else if (m <= 32 && one_round_192)
+    rc = launch_bf16_cfg<Cfg<192, 32, 4, 1, 64, 2, true>>(xb, m, k, wb, n, ob, ld, col_offset, st, 1, cu, n_tokens, pick);
   else if (m <= 32)
     rc = launch_bf16_cfg<Cfg<128, 32, 4, 1, 64, 3, true>>(xb, m, k, wb, n, ob, ld, col_offset, st, 1, cu, n_tokens, pick);
+  else if (m <= 64 && one_round_192)
+    rc = launch_bf16_cfg<Cfg<192, 64, 4, 1, 64, 2, true>>(xb, m, k, wb, n, ob, ld, col_offset, st, 1, cu, n_tokens, pick);
   else if (m <= 64)
     rc = launch_bf16_cfg<Cfg<128, 64, 4, 1, 64, 3, true>>(xb, m, k, wb, n, ob, ld, col_offset, st, 1, cu, n_tokens, pick);
   else if (m <= 128 || !direct_ok)
