@@ -783,9 +783,10 @@ def test_lmhead_decode_rows(name, m):
     _decode_rows(name, m)
 
 
-@pytest.mark.parametrize("m", [1, 5, 16, 24, 32, 48, 64])
+@pytest.mark.parametrize("m", [1, 5, 16, 24, 32, 48, 64, 96, 128])
 def test_lmhead_decode_rows_tp2_shard(m):
-    # the 75968-row shard takes 192-row decode tiles (one round over the CUs)
+    # the 75968-row shard takes 192-row decode tiles and 320 x 128 tiles up to
+    # M = 128 (one round over the CUs)
     _decode_rows("qwen3_0p6b_tp2_rank0", m)
 
 

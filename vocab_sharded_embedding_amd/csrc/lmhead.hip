@@ -1104,9 +1104,8 @@ int launch_lmhead(const void *x, int64_t m, int64_t k, const void *w, int64_t n,
   // Tile shapes by the number of hidden rows M (measured on MI355X):
   //  - M <= 64 (decode-size batches): the LM head streams W once and is
   //    bound by HBM, so tiles are narrow and there are many of them, with
-  //    three or four LDS stages keeping W loads well ahead of the MFMAs.
-  //    M <= 16:
-  //    64 vocabulary rows with 128-wide k steps (a sweep over tile heights
+  //    two to four LDS stages keeping W loads well ahead of the MFMAs.
+  //    M <= 16: 64 vocabulary rows with 128-wide k steps (a sweep over tile heights
   //    32-192, k steps 64/128 and 3-6 stages found it best or within 2% on
   //    75968- and 151936-row tables at D = 1024 and on 37984 x 4096).
   //    M <= 32: 128-row tiles, or 64-row ones when there would be fewer
@@ -1116,7 +1115,13 @@ int launch_lmhead(const void *x, int64_t m, int64_t k, const void *w, int64_t n,
   //    fused prefill select at M = 32: 3%).  Where 192-row tiles fit one
   //    round at two workgroups per CU (a 75968 x 1024 shard), they replace
   //    the 64- and 128-row ones: 4-10% faster for M = 16-64 there, within
-  //    1% at M = 1 and 8 (and slower on the full table, where they do not);
+  //    1% at M = 1 and 8 (and slower on the full table, where they do not).
+  //    25 <= M <= 32 takes them on long tables too (the full 151936-row
+  //    table: 2-3% faster, the fused prefill select included; at M = 24
+  //    they were 3% slower there);
+  //  - 64 < M <= 128: 256 x 128 tiles over 8 waves, three stages, or
+  //    320 x 128 with two stages where that fits one round and 256 rows do
+  //    not (the 75968-row shard: 20% faster at M = 96 and 128);
   //  - 128 < M <= 256: 320 vocabulary rows x 256 hidden rows over 8 waves
   //    (a wave owns 160 x 64), W and X both staged through two LDS stages.
   //    A 75968-row shard is 238 W tiles: one round over 256 CUs, with 0.35
@@ -1134,13 +1139,16 @@ int launch_lmhead(const void *x, int64_t m, int64_t k, const void *w, int64_t n,
   // fit one round over the 256 CUs at two per CU, e.g. a 75968-row shard
   // (396 tiles, where 128-row tiles spill 82 tiles into a second round)
   const bool one_round_192 = !few_tiles && (n + 191) / 192 <= 2 * 256;
+  // 320 x 128 tiles (one workgroup per CU) when 256-row ones would spill past
+  // one round and 320-row ones fit it (the 75968-row shard: 238 tiles)
+  const bool one_round_320 = direct_ok && (n + 255) / 256 > 256 && (n + 319) / 320 <= 256;
   if (m <= 16 && one_round_192)
     rc = launch_bf16_cfg<Cfg<192, 16, 4, 1, 64, 2, true>>(xb, m, k, wb, n, ob, ld, col_offset, st, 1, cu, n_tokens, pick);
   else if (m <= 16)
     rc = launch_bf16_cfg<Cfg<64, 16, 4, 1, 128, 4, true>>(xb, m, k, wb, n, ob, ld, col_offset, st, 1, cu, n_tokens, pick);
   else if (m <= 32 && few_tiles)
     rc = launch_bf16_cfg<Cfg<64, 32, 4, 1, 64, 4, true>>(xb, m, k, wb, n, ob, ld, col_offset, st, 1, cu, n_tokens, pick);
-  else if (m <= 32 && one_round_192)
+  else if (m <= 32 && (one_round_192 || m > 24))
     rc = launch_bf16_cfg<Cfg<192, 32, 4, 1, 64, 2, true>>(xb, m, k, wb, n, ob, ld, col_offset, st, 1, cu, n_tokens, pick);
   else if (m <= 32)
     rc = launch_bf16_cfg<Cfg<128, 32, 4, 1, 64, 3, true>>(xb, m, k, wb, n, ob, ld, col_offset, st, 1, cu, n_tokens, pick);
@@ -1148,6 +1156,8 @@ int launch_lmhead(const void *x, int64_t m, int64_t k, const void *w, int64_t n,
     rc = launch_bf16_cfg<Cfg<192, 64, 4, 1, 64, 2, true>>(xb, m, k, wb, n, ob, ld, col_offset, st, 1, cu, n_tokens, pick);
   else if (m <= 64)
     rc = launch_bf16_cfg<Cfg<128, 64, 4, 1, 64, 3, true>>(xb, m, k, wb, n, ob, ld, col_offset, st, 1, cu, n_tokens, pick);
+  else if (m <= 128 && one_round_320)
+    rc = launch_bf16_cfg<Cfg<320, 128, 4, 2, 64, 2>>(xb, m, k, wb, n, ob, ld, col_offset, st, 1, cu, n_tokens, pick);
   else if (m <= 128 || !direct_ok)
     // (operands that cannot take 16-byte loads go through registers; the
     // 256 x 128 tile keeps that path free of spills)
