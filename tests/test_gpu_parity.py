@@ -777,13 +777,13 @@ def test_parallel_lmhead_layer_fold_argmax():
 # ---------------------------------------------------------------------------
 # decode-size LM heads (a handful of rows against a whole shard)
 # ---------------------------------------------------------------------------
-@pytest.mark.parametrize("m", [1, 2, 5, 8, 16])
+@pytest.mark.parametrize("m", [1, 2, 5, 8, 16, 25, 32])
 @pytest.mark.parametrize("name", ["qwen3_0p6b_tp1_prefill", "large_v151936_d4096_tp4_rank2"])
 def test_lmhead_decode_rows(name, m):
     _decode_rows(name, m)
 
 
-@pytest.mark.parametrize("m", [1, 5, 16, 24, 32, 48, 64, 96, 128])
+@pytest.mark.parametrize("m", [1, 5, 16, 17, 24, 25, 32, 33, 48, 64, 65, 96, 128, 129])
 def test_lmhead_decode_rows_tp2_shard(m):
     # the 75968-row shard takes 192-row decode tiles and 320 x 128 tiles up to
     # M = 128 (one round over the CUs)
