@@ -171,6 +171,19 @@ def recorded_traffic(workload: str, kind: str):
         return None
 
 
+def traffic_key(workload: str, kind: str, lm_rows_override: int = 0,
+                unfused_prefill: bool = False) -> str:
+    """Workload name under which counter traffic of one kernel kind is recorded:
+    the LM-head kinds (and the separate select) depend on the LM-head rows and
+    on whether the prefill select is fused, the lookup and the sum do not."""
+    if kind.startswith("lmhead") or kind == "select":
+        if lm_rows_override:
+            workload += f"@m{lm_rows_override}"
+        if unfused_prefill:
+            workload += "@unfused"
+    return workload
+
+
 def algorithmic_bytes(w, ids, ranks_owned, fused_prefill=False, argmax=False):
     """Bytes the method must move per step, by kernel kind."""
     s = w.elem_bytes
@@ -459,9 +472,16 @@ def main():
         # no events in the timed region: nothing measured the dominant kernel
         roof.update(achieved=None, frac=None, avg_launch_us=None,
                     note="--timed-events none: no events in the timed region")
-    roof["traffic"] = recorded_traffic(w.name, dom)
+    base_rows = wl.WORKLOADS[args.workload].lm_rows
+    lm_override = args.lm_rows if args.lm_rows and args.lm_rows != base_rows else 0
+    unfused = bool(w.seqs) and args.unfused_prefill
+
+    def counted(kind):
+        return recorded_traffic(traffic_key(w.name, kind, lm_override, unfused), kind)
+
+    roof["traffic"] = counted(dom)
     for kind in breakdown:
-        breakdown[kind]["hbm_bytes_counted"] = recorded_traffic(w.name, kind)
+        breakdown[kind]["hbm_bytes_counted"] = counted(kind)
 
     # ---------------- CPU baseline: the oracle on the same workload ----------------
     cpu = None

@@ -94,3 +94,16 @@ def test_source_digest_ignores_comments_and_spacing(tmp_path):
 
 def test_unknown_traffic_record_is_none():
     assert bench.recorded_traffic("no_such_workload", "lmhead") is None
+
+
+def test_traffic_key_follows_the_lm_head_configuration():
+    k = bench.traffic_key
+    assert k("qwen3_0p6b_tp2_rank0", "lmhead") == "qwen3_0p6b_tp2_rank0"
+    assert k("qwen3_0p6b_tp2_rank0", "lmhead", 16) == "qwen3_0p6b_tp2_rank0@m16"
+    assert k("qwen3_0p6b_tp2_rank0", "lmhead_argmax", 8) == "qwen3_0p6b_tp2_rank0@m8"
+    assert k("qwen3_0p6b_tp2_rank0", "embed", 16) == "qwen3_0p6b_tp2_rank0"  # same lookup
+    assert k("qwen3_0p6b_tp1_prefill", "lmhead", 0, True) == "qwen3_0p6b_tp1_prefill@unfused"
+    assert k("qwen3_0p6b_tp1_prefill", "select", 0, True) == "qwen3_0p6b_tp1_prefill@unfused"
+    assert k("qwen3_0p6b_tp1_prefill", "embed", 0, True) == "qwen3_0p6b_tp1_prefill"
+    # a configuration whose counters were never recorded reports none
+    assert bench.recorded_traffic(k("qwen3_0p6b_tp2_rank0", "lmhead", 3), "lmhead") is None
