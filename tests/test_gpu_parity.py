@@ -808,6 +808,33 @@ def _decode_rows(name, m):
 
 
 # ---------------------------------------------------------------------------
+# a table past 2 GiB: row offsets beyond the 32-bit range
+# ---------------------------------------------------------------------------
+def test_table_past_2gib():
+    n, k, seed = 140000, 8192, 77  # 2.29 GB of bf16; row 131072 starts at byte 2^31
+    w_d = torch.empty((n, k), dtype=torch.bfloat16, device=dev())
+    for lo in range(0, n, 16384):
+        hi = min(n, lo + 16384)
+        w_d[lo:hi] = to_dev(wl.table_rows(seed, n, k, "bf16", lo, hi, std=0.5))
+    ranges = [(0, 32), (131040, 131104), (n - 64, n)]
+    cols = np.concatenate([np.arange(a, b) for a, b in ranges])
+    w_cols = np.concatenate([wl.table_rows(seed, n, k, "bf16", a, b, std=0.5) for a, b in ranges])
+    for m in (4, 300):
+        _say(f"table past 2 GiB: lmhead M={m}")
+        x = wl.hidden_states(900 + m, m, k, "bf16")
+        got = to_host(vpe.vpe_lmhead(to_dev(x), w_d))
+        assert_logits_close(got[:, cols], oracle.lmhead_f64(x, w_cols, nthreads=oracle_threads()),
+                            f"past 2 GiB M={m}")
+    _say("table past 2 GiB: lookup")
+    ids = np.concatenate([cols, [131071, 131072, n - 1, n, -1]]).astype(np.int64)
+    out = to_host(vpe.vpe_embed(to_dev(ids), w_d, 0))
+    assert out[:len(cols)].tobytes() == w_cols.tobytes()
+    assert np.all(out[-2:] == 0)  # ids n and -1 are outside the table
+    del w_d
+    torch.cuda.empty_cache()
+
+
+# ---------------------------------------------------------------------------
 # shard loading on the device, and one tied table for both calls
 # ---------------------------------------------------------------------------
 def test_load_shard_full_vocab_every_rank():
