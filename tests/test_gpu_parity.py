@@ -995,6 +995,36 @@ def test_graph_replays_match_eager():
     assert to_host(eb[1]).tobytes() == oracle.embed(to_host(ids_d), full, 0).tobytes()
 
 
+def test_graph_decode_loop_with_clearing_decode():
+    # a captured decode step (every shard's fold, then the clearing decode)
+    # replayed as a loop: the keys are set once, eagerly, before the loop, and
+    # each replay leaves them cleared for the next one (no init in the graph)
+    V, D, tp, m = 4096, 128, 2, 24
+    _, W = _int_inputs(810, 1, V, D, "bf16")
+    shards = [to_dev(W[r * V // tp:(r + 1) * V // tp]) for r in range(tp)]
+    starts = [r * V // tp for r in range(tp)]
+    x_d = torch.zeros((m, D), dtype=torch.bfloat16, device=dev())
+    best = torch.empty(m, dtype=torch.int64, device=dev())
+    vpe.vpe_argmax_init(best)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream(device=dev())
+    with torch.cuda.graph(g, stream=side):
+        for r in range(tp):
+            vpe.vpe_lmhead_argmax(x_d, shards[r], starts[r], best)
+        val, tok = vpe.vpe_argmax_decode_clear(best)
+    for step in range(4):
+        X, _ = _int_inputs(820 + step, m, 1, D, "bf16")
+        x_d.copy_(to_dev(X))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        ref_max, ref_idx = oracle.argmax_rows(oracle.lmhead_f64(X, W))
+        assert np.array_equal(to_host(tok), ref_idx), f"step {step}"
+        assert np.array_equal(to_host(val).astype(np.float64), ref_max), f"step {step}"
+        assert int(torch.count_nonzero(best)) == 0, f"step {step}"
+
+
 # ---------------------------------------------------------------------------
 # seeded random shapes: every kernel variant's edges, many times over
 # ---------------------------------------------------------------------------
