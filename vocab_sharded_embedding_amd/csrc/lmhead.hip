@@ -759,7 +759,8 @@ __device__ __forceinline__ void xreg_load_x(const uint16_t *x, int bytes, bf16x8
 // and a W fragment read from LDS feeds the wave's 2 X fragments while each
 // X fragment feeds 20 MFMAs from its register.  Measured on MI355X it is the
 // faster kernel once M spans several 256-row tiles (8-10% over the two-stage
-// kernel at M = 1024 and 4096); at M = 256 it is 5-7% slower.
+// kernel at M = 1024 and 4096); at M = 256 the two are even in the lookup-
+// then-LM-head step (5-7% apart, the other way, in back-to-back launches).
 // Requires 16-byte-aligned X and W with K % 8 == 0 (checked by the launcher).
 // ---------------------------------------------------------------------------
 template <int BN, int WV, int TM, int NS, bool GX, bool ARGMAX>
