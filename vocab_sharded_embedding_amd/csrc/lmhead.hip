@@ -1122,7 +1122,8 @@ int launch_lmhead(const void *x, int64_t m, int64_t k, const void *w, int64_t n,
   //    they were 3% slower there);
   //  - 64 < M <= 128: 256 x 128 tiles over 8 waves, three stages, or
   //    320 x 128 with two stages where that fits one round and 256 rows do
-  //    not (the 75968-row shard: 20% faster at M = 96 and 128);
+  //    not (the 75968-row shard: 20% faster at M = 96 and 128), its W read
+  //    once and so loaded non-temporally (another 6% in the step);
   //  - 128 < M <= 256: 320 vocabulary rows x 256 hidden rows over 8 waves
   //    (a wave owns 160 x 64), W and X both staged through two LDS stages.
   //    A 75968-row shard is 238 W tiles: one round over 256 CUs, with 0.35
@@ -1158,7 +1159,7 @@ int launch_lmhead(const void *x, int64_t m, int64_t k, const void *w, int64_t n,
   else if (m <= 64)
     rc = launch_bf16_cfg<Cfg<128, 64, 4, 1, 64, 3, true>>(xb, m, k, wb, n, ob, ld, col_offset, st, 1, cu, n_tokens, pick);
   else if (m <= 128 && one_round_320)
-    rc = launch_bf16_cfg<Cfg<320, 128, 4, 2, 64, 2>>(xb, m, k, wb, n, ob, ld, col_offset, st, 1, cu, n_tokens, pick);
+    rc = launch_bf16_cfg<Cfg<320, 128, 4, 2, 64, 2, true>>(xb, m, k, wb, n, ob, ld, col_offset, st, 1, cu, n_tokens, pick);
   else if (m <= 128 || !direct_ok)
     // (operands that cannot take 16-byte loads go through registers; the
     // 256 x 128 tile keeps that path free of spills)
