@@ -12,6 +12,7 @@
 
 #include "../../include/vpe.h"
 #include "stub_record.h"
+#include "../../vocab_sharded_embedding_amd/csrc/vpe_bounds.h"
 
 extern "C" {
 int orc_shard_range(int64_t, int32_t, int32_t, int64_t *, int64_t *);
@@ -190,7 +191,41 @@ static void check_oracle() {
   EXPECT(orc_load_shard(table.data(), V, D, 0, 4, 0, shard.data()) != 0);
 }
 
+// The LM-head launchers' choice between buffer loads (masked loads at byte
+// offset kLoadMask must read zeros, so a descriptor may cover at most
+// kLoadMask bytes) and element-wise register staging, at the edges of the
+// window (kLoadMask, 2^31) of gathered prefill activations.
+static void check_load_paths() {
+  using vpe::bf16_direct_loads_ok;
+  using vpe::bf16_rows_fit_descriptor;
+  using vpe::kLoadMask;
+  EXPECT(kLoadMask == 0x7FFF0000);
+  // K = 1024: 2048-byte rows; kLoadMask / 2048 = 1048544 rows exactly
+  EXPECT(bf16_rows_fit_descriptor(1048544, 1024));
+  EXPECT(!bf16_rows_fit_descriptor(1048545, 1024));
+  EXPECT(!bf16_rows_fit_descriptor(1048575, 1024));  // 2^31 - 2048 bytes: inside the window
+  EXPECT(!bf16_rows_fit_descriptor(1048576, 1024));  // 2^31 bytes
+  EXPECT(bf16_rows_fit_descriptor(0, 1024) && bf16_rows_fit_descriptor(5, 0));
+  EXPECT(!bf16_rows_fit_descriptor(-1, 8));
+  EXPECT(!bf16_rows_fit_descriptor(INT64_MAX, 8) && !bf16_rows_fit_descriptor(2, INT64_MAX / 2));
+  EXPECT(!bf16_rows_fit_descriptor(1, INT64_MAX) && bf16_rows_fit_descriptor(1, kLoadMask / 2));
+  // K = 4096 (8 KB rows): kLoadMask / 8192 = 262136 rows
+  EXPECT(bf16_rows_fit_descriptor(262136, 4096) && !bf16_rows_fit_descriptor(262137, 4096));
+  // gathered X: the whole token range counts, not the tile
+  EXPECT(bf16_direct_loads_ok(0x1000, 0x2000, 1024, true, 1048544, 32, 192));
+  EXPECT(!bf16_direct_loads_ok(0x1000, 0x2000, 1024, true, 1048545, 32, 192));
+  EXPECT(!bf16_direct_loads_ok(0x1000, 0x2000, 1024, true, 1048560, 32, 192));
+  // contiguous X: only the tile's rows count
+  EXPECT(bf16_direct_loads_ok(0x1000, 0x2000, 1024, false, 1048560, 256, 320));
+  EXPECT(bf16_direct_loads_ok(0x1000, 0x2000, 1 << 20, false, 0, 256, 320));
+  // alignment and K
+  EXPECT(!bf16_direct_loads_ok(0x1008, 0x2000, 1024, false, 0, 256, 320));
+  EXPECT(!bf16_direct_loads_ok(0x1000, 0x2002, 1024, false, 0, 256, 320));
+  EXPECT(!bf16_direct_loads_ok(0x1000, 0x2000, 1020, false, 0, 256, 320));
+}
+
 int main() {
+  check_load_paths();
   check_abi();
   check_oracle();
   if (!g_fail) printf("host sanitizer driver: all expectations held\n");

@@ -31,6 +31,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "vpe_bounds.h"
 #include "vpe_launch.h"
 
 namespace vpe {
@@ -121,8 +122,9 @@ __device__ __forceinline__ int lds_piece_offset(int row, int piece) {
 }
 
 // Offset past any descriptor's range: buffer loads at it return zeros.  Every
-// descriptor built here covers at most kBig bytes.
-constexpr int kBig = 0x7FFF0000;
+// descriptor built here covers at most kBig bytes (the launchers check it
+// with bf16_direct_loads_ok before they take the buffer-load paths).
+constexpr int kBig = kLoadMask;
 
 // Writes a wave's accumulators.  acc[i][j][r] = Z^T[n][m] for the vocabulary
 // row n = nb + 16 i + r and hidden row m = mb + 16 j, where nb and mb are the
@@ -1023,11 +1025,12 @@ int launch_bf16_cfg(const uint16_t *x, int64_t m, int64_t k, const uint16_t *w, 
   const int tiles_m = static_cast<int>(tm64);
   const dim3 grid(static_cast<unsigned>(tiles_n) * static_cast<unsigned>(tiles_m));
   const bool gx = cu != nullptr;
-  // 16-byte buffer loads need 16-byte rows and bases, and every byte offset of
-  // a gathered X row must fit the descriptor's 32-bit range
-  const bool vec = (k % 8 == 0) &&
-                   ((reinterpret_cast<uint64_t>(x) | reinterpret_cast<uint64_t>(w)) & 15) == 0 &&
-                   (!gx || n_tokens * k * 2 < (int64_t(1) << 31));
+  // 16-byte buffer loads need 16-byte rows and bases, and every descriptor
+  // (the W tile, the X tile or all gathered tokens) must end at or before the
+  // masked-load offset, so that masked loads read zeros
+  const bool vec = bf16_direct_loads_ok(reinterpret_cast<uint64_t>(x),
+                                        reinterpret_cast<uint64_t>(w), k, gx, n_tokens, C::BM,
+                                        C::BN);
 #define VPE_LAUNCH(V, G)                                                                     \
   do {                                                                                       \
     if (pick.best)                                                                           \
@@ -1056,10 +1059,9 @@ bool launch_bf16_xreg(const uint16_t *x, int64_t m, int64_t k, const uint16_t *w
                       uint16_t *out, int64_t ld, int64_t col_off, hipStream_t st, int group_n,
                       const int32_t *cu, int64_t n_tokens, ArgmaxOut pick, int *rc) {
   const bool gx = cu != nullptr;
-  const bool vec = (k % 8 == 0) &&
-                   ((reinterpret_cast<uint64_t>(x) | reinterpret_cast<uint64_t>(w)) & 15) == 0 &&
-                   (gx ? n_tokens * k * 2 <= kBig : int64_t(WV * TM) * k * 2 <= kBig) &&
-                   int64_t(BN) * k * 2 <= kBig;
+  const bool vec = bf16_direct_loads_ok(reinterpret_cast<uint64_t>(x),
+                                        reinterpret_cast<uint64_t>(w), k, gx, n_tokens, WV * TM,
+                                        BN);
   if (!vec) return false;
   const int64_t tn64 = (n + BN - 1) / BN, tm64 = (m + WV * TM - 1) / (WV * TM);
   if (tn64 * tm64 > INT32_MAX) {
@@ -1132,9 +1134,12 @@ int launch_lmhead(const void *x, int64_t m, int64_t k, const void *w, int64_t n,
   //    W stages in LDS; tiles ordered in groups of 8 W tiles, so that an
   //    XCD's ~32 concurrent tiles share 8 W tiles and 4 X tiles in its L2
   //    (groups of 8 measured 5-7% faster than groups of 2 or 4 at M = 4096).
-  // 16-byte loads straight to LDS need K % 8 == 0 and 16-byte-aligned bases
-  const bool direct_ok =
-      k % 8 == 0 && ((reinterpret_cast<uint64_t>(x) | reinterpret_cast<uint64_t>(w)) & 15) == 0;
+  // 16-byte loads straight to LDS need K % 8 == 0, 16-byte-aligned bases and
+  // descriptors that end before the masked-load offset (every tile below has
+  // at most 320 W rows and 256 X rows; gathered X spans all n_tokens rows)
+  const bool direct_ok = bf16_direct_loads_ok(reinterpret_cast<uint64_t>(x),
+                                              reinterpret_cast<uint64_t>(w), k, cu != nullptr,
+                                              n_tokens, 256, 320);
   int rc;
   const bool few_tiles = (n + 127) / 128 < 512;
   // 192-row decode tiles (two LDS stages, two workgroups per CU) when they
