@@ -33,15 +33,34 @@ class OracleError(RuntimeError):
     pass
 
 
+_CMD = ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-pthread",
+        "-fno-fast-math", "-ffp-contract=off", "-Wall", "-Wextra"]
+
+
+def _digest() -> str:
+    """sha256 of oracle.c and the compile command."""
+    import hashlib
+    with open(_SRC, "rb") as f:
+        return hashlib.sha256(f.read() + " ".join(_CMD).encode()).hexdigest()
+
+
 def build(force: bool = False) -> str:
-    """Compile oracle.c into liboracle.so with gcc (plain -O2, no fast-math)."""
-    if force or not os.path.exists(_LIB):
+    """Compile oracle.c into liboracle.so with gcc (plain -O2, no fast-math).
+    Also rebuilds when the library was built from another oracle.c (the digest
+    recorded next to it differs)."""
+    digest = _digest()
+    try:
+        with open(_LIB + ".sha256") as f:
+            current = f.read().strip() == digest and os.path.exists(_LIB)
+    except OSError:
+        current = False
+    if force or not current:
         tmp = _LIB + ".tmp%d" % os.getpid()
-        cmd = ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-pthread",
-               "-fno-fast-math", "-ffp-contract=off", "-Wall", "-Wextra",
-               _SRC, "-o", tmp]
-        subprocess.run(cmd, check=True)
+        subprocess.run(_CMD + [_SRC, "-o", tmp], check=True)
         os.replace(tmp, _LIB)
+        with open(_LIB + ".sha256.tmp%d" % os.getpid(), "w") as f:
+            f.write(digest + "\n")
+        os.replace(_LIB + ".sha256.tmp%d" % os.getpid(), _LIB + ".sha256")
     return _LIB
 
 

@@ -273,3 +273,52 @@ def test_load_shard_validation():
     # rank 1's rows start at byte 50*8*2 = 800: a shard at FAKE + 1000 overlaps them
     assert f(FAKE, 100, 8, BF16, 2, 1, FAKE + 1000, None) == vpe.VPE_ERR_RANGE
     assert f(FAKE, 100, 8, BF16, 2, 0, FAKE + 16, None) == vpe.VPE_ERR_RANGE
+
+
+# ---------------------------------------------------------------------------
+# a library built from other sources is refused, not loaded silently
+# ---------------------------------------------------------------------------
+def test_built_library_matches_its_sources():
+    from vocab_sharded_embedding_amd import build as vbuild
+    assert vbuild.built_digest() == vbuild.source_digest()
+    vpe.check_library_current()
+
+
+def test_mismatched_digest_is_refused(tmp_path, monkeypatch):
+    import shutil
+    from vocab_sharded_embedding_amd import build as vbuild
+    lib = tmp_path / "libvpe.so"
+    shutil.copy(vpe.LIB_PATH, lib)
+    # no digest recorded at all
+    with pytest.raises(vpe.StaleLibraryError):
+        vpe.check_library_current(str(lib))
+    # a digest of other sources
+    (tmp_path / "libvpe.so.sha256").write_text("0" * 64 + "\n")
+    with pytest.raises(vpe.StaleLibraryError):
+        vpe.check_library_current(str(lib))
+    monkeypatch.setattr(vpe, "_lib", None)
+    monkeypatch.delenv("VPE_REBUILD_STALE", raising=False)
+    with pytest.raises(vpe.StaleLibraryError):
+        vpe.load_library(str(lib))
+    # the tree's own digest is accepted
+    (tmp_path / "libvpe.so.sha256").write_text(vbuild.source_digest() + "\n")
+    vpe.check_library_current(str(lib))
+
+
+def test_source_edit_changes_the_digest(tmp_path, monkeypatch):
+    from vocab_sharded_embedding_amd import build as vbuild
+    files = vbuild.source_files()
+    assert any(f.endswith("lmhead.hip") for f in files)
+    assert any(f.endswith("vpe.h") for f in files)
+    before = vbuild.source_digest()
+    # the same file list with one kernel source edited by one byte
+    edited = []
+    for f in files:
+        dst = tmp_path / os.path.basename(f)
+        data = open(f, "rb").read()
+        if f.endswith("gather.hip"):
+            data += b" "
+        dst.write_bytes(data)
+        edited.append(str(dst))
+    monkeypatch.setattr(vbuild, "source_files", lambda: edited)
+    assert vbuild.source_digest() != before

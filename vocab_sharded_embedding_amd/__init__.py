@@ -44,14 +44,40 @@ class VpeError(RuntimeError):
 _lib = None
 
 
+class StaleLibraryError(RuntimeError):
+    """libvpe.so was built from sources other than the ones next to it."""
+
+
+def check_library_current(path: str = LIB_PATH) -> None:
+    """Raise StaleLibraryError unless the digest recorded next to the library
+    when it was built equals the digest of the sources in this tree."""
+    from . import build as _build
+    have, want = _build.built_digest(path), _build.source_digest()
+    if have != want:
+        raise StaleLibraryError(
+            f"{path} does not match its sources (built from "
+            f"{have[:12] or 'unrecorded sources'}, tree is {want[:12]}): rebuild it with "
+            "`python -m vocab_sharded_embedding_amd.build` (or __graft_entry__.build()), "
+            "or set VPE_REBUILD_STALE=1 to rebuild on load")
+
+
 def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
-    """Load libvpe.so (building it first only if no build exists)."""
+    """Load libvpe.so.  It is built first when missing; a library whose recorded
+    source digest differs from the tree's sources is refused (StaleLibraryError),
+    or rebuilt when the environment sets VPE_REBUILD_STALE=1."""
     global _lib
     if _lib is not None:
         return _lib
+    from . import build as _build
     if not os.path.exists(path):
-        from . import build as _build
         _build.build()
+    try:
+        check_library_current(path)
+    except StaleLibraryError:
+        if os.environ.get("VPE_REBUILD_STALE") != "1" or path != LIB_PATH:
+            raise
+        _build.build()
+        check_library_current(path)
     lib = ctypes.CDLL(path)
     i64, i32, vp, ci = ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p, ctypes.c_int
     lib.vpe_shard_range.argtypes = [i64, i32, i32, ctypes.POINTER(i64), ctypes.POINTER(i64)]
@@ -370,5 +396,6 @@ __all__ = [
     "vpe_shard_range", "vpe_embed", "vpe_sum_partials", "vpe_last_token_select", "vpe_lmhead",
     "vpe_lmhead_prefill", "vpe_argmax_init", "vpe_lmhead_argmax", "vpe_lmhead_prefill_argmax",
     "vpe_argmax_decode", "vpe_argmax_decode_clear", "vpe_load_shard",
-    "VocabParallelEmbedding", "ParallelLMHead", "VpeError", "load_library", "LIB_PATH",
+    "VocabParallelEmbedding", "ParallelLMHead", "VpeError", "StaleLibraryError", "load_library",
+    "check_library_current", "LIB_PATH",
 ]

@@ -3,6 +3,7 @@ with g++ (it has no HIP dependency), linked into one shared library."""
 from __future__ import annotations
 
 import concurrent.futures as cf
+import hashlib
 import os
 import subprocess
 import sys
@@ -13,6 +14,7 @@ CSRC = os.path.join(PKG, "csrc")
 ROOT = os.path.dirname(PKG)
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libvpe.so")
+DIGEST = LIB + ".sha256"  # digest of the sources and flags the library was built from
 OBJDIR = os.path.join(PKG, "_build")
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
@@ -30,6 +32,35 @@ HIP_FLAGS = [
 CXX_FLAGS = ["-O2", "-fPIC", "-std=c++17", "-Wall", "-Wextra", "-I", INCLUDE, "-I", CSRC]
 
 
+def source_files() -> List[str]:
+    """Every file the library is built from: kernels, the C-ABI layer, the
+    internal headers, the public header and this build script."""
+    names = sorted(f for f in os.listdir(CSRC)
+                   if f.endswith((".hip", ".cpp", ".h")))
+    return [os.path.join(CSRC, f) for f in names] + [os.path.join(INCLUDE, "vpe.h"),
+                                                     os.path.abspath(__file__)]
+
+
+def source_digest() -> str:
+    """sha256 over the names and contents of source_files()."""
+    h = hashlib.sha256()
+    for path in source_files():
+        with open(path, "rb") as f:
+            data = f.read()
+        h.update(os.path.basename(path).encode() + b"\0" + str(len(data)).encode() + b"\0")
+        h.update(data)
+    return h.hexdigest()
+
+
+def built_digest(lib: str = LIB) -> str:
+    """The digest recorded next to a built library ('' when none is)."""
+    try:
+        with open(lib + ".sha256") as f:
+            return f.read().strip()
+    except OSError:
+        return ""
+
+
 def _run(cmd: List[str]) -> None:
     r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
     # hipcc's host pass does not know the packed-fp32 feature and says so: harmless
@@ -44,6 +75,7 @@ def _run(cmd: List[str]) -> None:
 def build(verbose: bool = False) -> str:
     """Compile every source and link libvpe.so; returns the library path."""
     os.makedirs(OBJDIR, exist_ok=True)
+    digest = source_digest()  # taken before compiling: a later edit makes it stale
     jobs = []
     objs = []
     for src in HIP_SOURCES:
@@ -63,6 +95,9 @@ def build(verbose: bool = False) -> str:
     _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-Wl,--no-undefined", *objs,
           "-o", tmp])
     os.replace(tmp, LIB)
+    with open(DIGEST + ".tmp", "w") as f:
+        f.write(digest + "\n")
+    os.replace(DIGEST + ".tmp", DIGEST)
     if verbose:
         print(f"built {LIB}")
     return LIB
