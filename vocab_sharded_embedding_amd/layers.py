@@ -53,7 +53,7 @@ class VocabParallelEmbedding(torch.nn.Module):
                 and loaded_weight.dtype == param.data.dtype):
             vpe_load_shard(loaded_weight, self.tp_size, self.tp_rank, out=param.data)
             return
-        piece = loaded_weight.narrow(0, self.tp_rank * shard, shard)
+        piece = loaded_weight.narrow(0, self.vocab_start_idx, shard)
         if piece.shape != param.data.shape:
             raise ValueError(f"loaded table slice {tuple(piece.shape)} does not match "
                              f"shard {tuple(param.data.shape)}")
