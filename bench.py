@@ -20,6 +20,13 @@ stream around its launches inside the timed region, the only events there
 (timing-only events without the system-scope fence, see TimingEvent).
 The per-kernel breakdown comes from a separate, untimed pass with events
 around every call.
+
+After the default step, the same process times every other workload at its
+own size (the fused prefill, both tp=2 ranks concatenated, the hidden-4096
+shard) and the default shard's LM head at decode batches of 1 and 16 rows,
+each the same way, and reports them under "workloads": per configuration the
+step time and, per kernel, its launch time and its fraction of the roofline
+that bounds it (HBM bandwidth, or dense bf16 MFMA past the ridge point).
 """
 from __future__ import annotations
 
@@ -73,6 +80,10 @@ def parse_args():
     p.add_argument("--no-breakdown", action="store_true",
                    help="skip the separate per-call event pass (a diagnostic run: a kernel "
                         "trace then holds only the warmup and timed steps)")
+    p.add_argument("--no-extra-workloads", action="store_true",
+                   help="time only the chosen step; by default the unmodified default step is "
+                        "followed by every other workload and two decode batch sizes, reported "
+                        "under \"workloads\"")
     p.add_argument("--copy-probe-mib", type=int, default=0,
                    help="after timing, run one device-to-device copy of this many MiB "
                         "(a reference kernel for hardware byte counters)")
@@ -212,6 +223,28 @@ def algorithmic_bytes(w, ids, ranks_owned, fused_prefill=False, argmax=False):
     return out, flops
 
 
+# Configurations timed in the same process after the headline one and
+# reported under "workloads": every other workload at its own size, and the
+# default shard's LM head at two decode batch sizes (workload name, LM rows or
+# 0 for the workload's own).
+EXTRA_RUNS = (
+    ("qwen3_0p6b_tp1_prefill", 0),
+    ("qwen3_0p6b_tp2_all_ranks", 0),
+    ("large_v151936_d4096_tp4_rank2", 0),
+    ("qwen3_0p6b_tp2_rank0", 1),
+    ("qwen3_0p6b_tp2_rank0", 16),
+)
+
+
+def kernel_bound(kind, dtype, nbytes, nflops):
+    """The roofline that bounds one launch: 'mfma' for a bf16 contraction past
+    the ridge point (flops / bytes above peak flops / peak bytes), else 'hbm'."""
+    ridge = (BF16_MFMA_PEAK_TFLOPS * 1e12) / (HBM_PEAK_GBS * 1e9)
+    if dtype == "bf16" and nflops and nbytes and nflops / nbytes > ridge:
+        return "mfma"
+    return "hbm"
+
+
 def main():
     args = parse_args()
     if args.gpus != 1:
@@ -219,7 +252,6 @@ def main():
               "(tensor-parallel ranks are emulated on one device)", file=sys.stderr)
         sys.exit(2)
 
-    import numpy as np
     import torch
 
     import vocab_sharded_embedding_amd as vpe
@@ -241,17 +273,114 @@ def main():
         w = dataclasses.replace(w, lm_rows=args.lm_rows)
     dev = torch.device("cuda:0")
     lib = vpe.load_library()
-    tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
-    s = w.elem_bytes
+
+    if args.load_shard:
+        return bench_load_shard(args, w, lib, dev, _uploader(torch, dev))
+
+    res = measure(args, w, lib, dev, argmax=args.argmax, unfused_prefill=args.unfused_prefill,
+                  timed_events=args.timed_events, breakdown=not args.no_breakdown,
+                  library_gemm=args.library_gemm, copy_probe_mib=args.copy_probe_mib,
+                  lm_override=args.lm_rows, with_cpu=not args.no_cpu_baseline)
+
+    extras = None
+    if want_extra_runs(args):
+        extras = {}
+        for name, rows in EXTRA_RUNS:
+            we = wl.WORKLOADS[name]
+            if rows:
+                import dataclasses
+                we = dataclasses.replace(we, lm_rows=rows)
+            key = name + (f"@m{rows}" if rows else "")
+            r = measure(args, we, lib, dev, argmax=False, unfused_prefill=False,
+                        timed_events="dominant", breakdown=True, library_gemm=False,
+                        copy_probe_mib=0, lm_override=rows, with_cpu=False)
+            extras[key] = summarize_extra(r)
+            torch.cuda.empty_cache()
+
+    w = res["w"]
+    line = {
+        "metric": METRIC, "value": round(res["value"], 2), "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(res["ms_per_step"], 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": w.dtype, "data": "synthetic",
+        "config": {"workload": w.name, "vocab": w.vocab, "dim": w.dim, "tp": w.tp,
+                   "ranks": list(w.ranks), "n_ids": res["n_ids"], "id_dist": w.id_dist,
+                   "lm_rows": w.lm_rows, "seqs": w.seqs, "concat": w.concat,
+                   "rotating_copies": res["copies"],
+                   "prefill_select": ("fused" if res["fused_prefill"] else "separate")
+                   if w.seqs else None,
+                   "lm_output": "argmax" if args.argmax else "logits",
+                   "step_algorithmic_bytes": res["step_bytes"]},
+        "roofline": res["roofline"],
+        "cpu_baseline": res["cpu_baseline"],
+        "breakdown": res["breakdown"],
+        "workloads": extras,
+        "library_gemm": res["library_gemm"],
+        "device": torch.cuda.get_device_name(dev),
+        "input_gen_s": round(res["gen_s"], 2),
+    }
+    print(json.dumps(line), flush=True)
+
+
+def want_extra_runs(args) -> bool:
+    """The other configurations run only with the default, unmodified step
+    (diagnostic and single-workload runs, e.g. under a profiler, skip them)."""
+    return (not args.no_extra_workloads and args.workload == DEFAULT_WORKLOAD
+            and not args.lm_rows and not args.argmax and not args.unfused_prefill
+            and args.timed_events == "dominant" and not args.no_breakdown
+            and not args.library_gemm and not args.copy_probe_mib)
+
+
+def summarize_extra(r) -> dict:
+    """One configuration's entry under "workloads": the step, and per kernel its
+    launch time, rate and fraction of the roofline that bounds it."""
+    w = r["w"]
+    kernels = {}
+    for kind, e in r["breakdown"].items():
+        k = {"bound": e["bound"], "us_per_launch": e["us_per_launch"],
+             "frac": e["frac"], "hbm_bytes_counted": e["hbm_bytes_counted"]}
+        k["GB_per_s"] = e["GB_per_s"]
+        if "TFLOP_per_s" in e:
+            k["TFLOP_per_s"] = e["TFLOP_per_s"]
+        if kind == "embed":
+            k["rows_per_s"] = e["rows_per_s"]
+        kernels[kind] = k
+    roof = r["roofline"]
+    return {"workload": w.name, "lm_rows": w.lm_rows, "n_ids": r["n_ids"],
+            "rotating_copies": r["copies"], "ms_per_step": round(r["ms_per_step"], 5),
+            "step_GB_per_s": round(r["value"], 2),
+            "step_algorithmic_bytes": r["step_bytes"],
+            "dominant": {"kernel": roof["kernel"], "bound": roof["bound"],
+                         "avg_launch_us": roof["avg_launch_us"], "achieved": roof["achieved"],
+                         "unit": roof["unit"], "frac": roof["frac"],
+                         "traffic": roof["traffic"]},
+            "kernels": kernels}
+
+
+def _uploader(torch, dev):
+    import numpy as np
 
     def up(a):
         a = np.ascontiguousarray(a)
         if a.dtype == np.uint16:
             return torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
         return torch.from_numpy(a).to(dev)
+    return up
 
-    if args.load_shard:
-        return bench_load_shard(args, w, lib, dev, up)
+
+def measure(args, w, lib, dev, *, argmax, unfused_prefill, timed_events, breakdown,
+            library_gemm, copy_probe_mib, lm_override, with_cpu):
+    """Times args.steps steps of workload w (after args.warmup untimed ones) and
+    returns the step rate, the dominant kernel's roofline entry and a per-kernel
+    breakdown (see the module docstring for what is timed how)."""
+    import numpy as np
+    import torch
+
+    import vocab_sharded_embedding_amd as vpe
+    import workloads as wl
+
+    tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    up = _uploader(torch, dev)
 
     # ---------------- inputs (host, seeded) ----------------
     t0 = time.time()
@@ -274,7 +403,8 @@ def main():
     base = {"ids": up(ids_h), "hidden": up(hidden_h),
             "cu": up(cu_h) if cu_h is not None else None,
             "shards": {r: up(a) for r, a in shards_h.items()}}
-    del shards_h
+    if not with_cpu:
+        del shards_h
     sets = []
     for c in range(copies):
         d = {k: (v.clone() if torch.is_tensor(v) else v) for k, v in base.items() if k != "shards"}
@@ -285,7 +415,7 @@ def main():
                           if len(w.ranks) > 1 else d["partials"][0])
         d["x"] = (torch.empty((w.seqs, w.dim), dtype=tdt, device=dev) if w.seqs
                   else d["hidden"])
-        if args.argmax:
+        if argmax:
             d["best"] = torch.empty(M, dtype=torch.int64, device=dev)
             d["pick_val"] = torch.empty(M, dtype=torch.float32, device=dev)
             d["pick_tok"] = torch.empty(M, dtype=torch.int64, device=dev)
@@ -303,6 +433,7 @@ def main():
 
     stream = torch.cuda.current_stream(dev)
     sh = stream.cuda_stream
+    fused = bool(w.seqs) and not unfused_prefill
     calls = []  # per copy: list of (kind, fn, args)
     for d in sets:
         seq = []
@@ -316,19 +447,18 @@ def main():
             seq.append(("sum", lib.vpe_sum_partials,
                         (arr, len(w.ranks), ids_h.size * w.dim, dcode, d["embed_out"].data_ptr(),
                          sh)))
-        fused = bool(w.seqs) and not args.unfused_prefill
         if w.seqs and not fused:
             seq.append(("select", lib.vpe_last_token_select,
                         (d["hidden"].data_ptr(), hidden_h.shape[0], w.dim, dcode,
                          d["cu"].data_ptr(), w.seqs, d["x"].data_ptr(), sh)))
         for r in w.ranks:
-            if args.argmax and fused:
+            if argmax and fused:
                 # the greedy pick reads each sequence's last position itself
                 seq.append(("lmhead_argmax", lib.vpe_lmhead_prefill_argmax,
                             (d["hidden"].data_ptr(), hidden_h.shape[0], w.dim, d["cu"].data_ptr(),
                              w.seqs, d["shards"][r].data_ptr(), w.shard_rows, dcode,
                              w.rank_start(r), d["best"].data_ptr(), sh)))
-            elif args.argmax:
+            elif argmax:
                 seq.append(("lmhead_argmax", lib.vpe_lmhead_argmax,
                             (d["x"].data_ptr(), M, w.dim, d["shards"][r].data_ptr(), w.shard_rows,
                              dcode, w.rank_start(r), d["best"].data_ptr(), sh)))
@@ -344,16 +474,14 @@ def main():
                             (d["x"].data_ptr(), M, w.dim, d["shards"][r].data_ptr(), w.shard_rows,
                              dcode, d["logits"].data_ptr(), d["logits"].shape[1],
                              w.rank_start(r) if w.concat else 0, sh)))
-        if args.argmax:
+        if argmax:
             # the decode clears the keys it reads: the next step's folds need no init
             seq.append(("argmax_decode", lib.vpe_argmax_decode_clear,
                         (d["best"].data_ptr(), M, d["pick_val"].data_ptr(),
                          d["pick_tok"].data_ptr(), sh)))
         calls.append(seq)
 
-    fused_prefill = bool(w.seqs) and not args.unfused_prefill
-    bytes_, flops_ = algorithmic_bytes(w, ids_h, owned, fused_prefill=fused_prefill,
-                                       argmax=args.argmax)
+    bytes_, flops_ = algorithmic_bytes(w, ids_h, owned, fused_prefill=fused, argmax=argmax)
     step_bytes = sum(sum(v) for v in bytes_.values())
     # dominant kernel: most algorithmic bytes per step
     dom = max(bytes_, key=lambda k: sum(bytes_[k]))
@@ -377,7 +505,7 @@ def main():
                 for _ in kinds]
 
     with torch.cuda.stream(stream):
-        if args.argmax:
+        if argmax:
             # once per input copy, outside the steps: every step's decode leaves
             # its copy's keys cleared for that copy's next step
             for d in sets:
@@ -392,24 +520,24 @@ def main():
         evs = [new_events() for _ in range(args.steps)]
         torch.cuda.synchronize()
         t_start = time.perf_counter()
-        timed_idx = dom_idx if args.timed_events == "dominant" else ()
+        timed_idx = dom_idx if timed_events == "dominant" else ()
         for k in range(args.steps):
             run_step(k, evs[k], timed_idx)
         torch.cuda.synchronize()
         t_total = time.perf_counter() - t_start
         # per-kernel breakdown: a separate, untimed pass with every call bracketed
-        n_bd = 0 if args.no_breakdown else min(args.steps, 50)
+        n_bd = min(args.steps, 50) if breakdown else 0
         bd_evs = [new_events() for _ in range(n_bd)]
         for k in range(n_bd):
             run_step(k, bd_evs[k], range(len(kinds)))
         torch.cuda.synchronize()
 
     lib_gemm = None
-    if args.library_gemm and "lmhead" in kinds:
+    if library_gemm and "lmhead" in kinds:
         lib_gemm = library_gemm_reference(torch, sets, w, M, args, stream)
 
-    if args.copy_probe_mib:
-        src = torch.empty(args.copy_probe_mib << 20, dtype=torch.uint8, device=dev)
+    if copy_probe_mib:
+        src = torch.empty(copy_probe_mib << 20, dtype=torch.uint8, device=dev)
         dst = torch.empty_like(src)
         dst.copy_(src)
         torch.cuda.synchronize()
@@ -430,7 +558,14 @@ def main():
     ms_per_step = t_total * 1e3 / args.steps
     value = step_bytes / (ms_per_step * 1e-3) / 1e9
 
-    breakdown = {}
+    base_rows = wl.WORKLOADS[w.name].lm_rows
+    lm_key = lm_override if lm_override and lm_override != base_rows else 0
+    unfused = bool(w.seqs) and unfused_prefill
+
+    def counted(kind):
+        return recorded_traffic(traffic_key(w.name, kind, lm_key, unfused), kind)
+
+    breakdown_ = {}
     for kind, lst in per_kind_ms.items():
         us = [m * 1e3 for m in lst]
         b = bytes_[kind]
@@ -441,21 +576,23 @@ def main():
              "hbm_frac": [round(g / HBM_PEAK_GBS, 4) for g in gbs]}
         if kind == "embed":
             e["rows_per_s"] = [round(ids_h.size / (u * 1e-6), 1) for u in us]
-        if kind in flops_:
-            f = flops_[kind]
+        f = flops_.get(kind)
+        if f:
             tf = [ff / (u * 1e-6) / 1e12 for ff, u in zip(f, us)]
             e["TFLOP_per_s"] = [round(t, 2) for t in tf]
             peak = BF16_MFMA_PEAK_TFLOPS if w.dtype == "bf16" else FP32_VECTOR_PEAK_TFLOPS
             e["mfma_frac" if w.dtype == "bf16" else "fp32_frac"] = [round(t / peak, 4) for t in tf]
-        breakdown[kind] = e
+        e["bound"] = kernel_bound(kind, w.dtype, float(np.mean(b)),
+                                  float(np.mean(f)) if f else 0.0)
+        e["frac"] = e["mfma_frac"] if e["bound"] == "mfma" else e["hbm_frac"]
+        e["hbm_bytes_counted"] = counted(kind)
+        breakdown_[kind] = e
 
     # the dominant kernel's duration, from the events of the timed region
     dom_us = float(np.mean(dom_ms)) * 1e3 if dom_ms else float("nan")
     dom_bytes = float(np.mean(bytes_[dom]))
     dom_flops = float(np.mean(flops_.get(dom, [0])))
-    ai = dom_flops / dom_bytes if dom_bytes else 0.0
-    ridge = (BF16_MFMA_PEAK_TFLOPS * 1e12) / (HBM_PEAK_GBS * 1e9)
-    if dom in flops_ and ai > ridge:
+    if kernel_bound(dom, w.dtype, dom_bytes, dom_flops) == "mfma":
         ach = dom_flops / (dom_us * 1e-6) / 1e12
         roof = {"kernel": dom, "bound": "mfma", "achieved": round(ach, 2),
                 "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
@@ -472,42 +609,18 @@ def main():
         # no events in the timed region: nothing measured the dominant kernel
         roof.update(achieved=None, frac=None, avg_launch_us=None,
                     note="--timed-events none: no events in the timed region")
-    base_rows = wl.WORKLOADS[args.workload].lm_rows
-    lm_override = args.lm_rows if args.lm_rows and args.lm_rows != base_rows else 0
-    unfused = bool(w.seqs) and args.unfused_prefill
-
-    def counted(kind):
-        return recorded_traffic(traffic_key(w.name, kind, lm_override, unfused), kind)
-
     roof["traffic"] = counted(dom)
-    for kind in breakdown:
-        breakdown[kind]["hbm_bytes_counted"] = counted(kind)
 
     # ---------------- CPU baseline: the oracle on the same workload ----------------
     cpu = None
-    if not args.no_cpu_baseline:
-        cpu = cpu_baseline(w, ids_h, hidden_h, cu_h, step_bytes, args.cpu_threads)
-
-    line = {
-        "metric": METRIC, "value": round(value, 2), "unit": "GB/s", "n_gpus": 1,
-        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5),
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": w.dtype, "data": "synthetic",
-        "config": {"workload": w.name, "vocab": w.vocab, "dim": w.dim, "tp": w.tp,
-                   "ranks": list(w.ranks), "n_ids": int(ids_h.size), "id_dist": w.id_dist,
-                   "lm_rows": M, "seqs": w.seqs, "concat": w.concat, "rotating_copies": copies,
-                   "prefill_select": ("fused" if fused_prefill else "separate")
-                   if w.seqs else None,
-                   "lm_output": "argmax" if args.argmax else "logits",
-                   "step_algorithmic_bytes": step_bytes},
-        "roofline": roof,
-        "cpu_baseline": cpu,
-        "breakdown": breakdown,
-        "library_gemm": lib_gemm,
-        "device": torch.cuda.get_device_name(dev),
-        "input_gen_s": round(gen_s, 2),
-    }
-    print(json.dumps(line), flush=True)
+    if with_cpu:
+        cpu = cpu_baseline(w, ids_h, hidden_h, cu_h, step_bytes, args.cpu_threads,
+                           shards=shards_h)
+    del sets, calls
+    return {"w": w, "value": value, "ms_per_step": ms_per_step, "step_bytes": step_bytes,
+            "roofline": roof, "breakdown": breakdown_, "cpu_baseline": cpu,
+            "library_gemm": lib_gemm, "copies": copies, "fused_prefill": fused,
+            "n_ids": int(ids_h.size), "gen_s": gen_s}
 
 
 def library_gemm_reference(torch, sets, w, M, args, stream):
@@ -622,7 +735,7 @@ def bench_load_shard(args, w, lib, dev, up):
     print(json.dumps(line), flush=True)
 
 
-def cpu_baseline(w, ids_h, hidden_h, cu_h, step_bytes, threads):
+def cpu_baseline(w, ids_h, hidden_h, cu_h, step_bytes, threads, shards=None):
     """The oracle, as it stands, on the same step (bounded: one pass)."""
     import numpy as np
 
@@ -630,7 +743,8 @@ def cpu_baseline(w, ids_h, hidden_h, cu_h, step_bytes, threads):
     import workloads as wl
 
     nt = threads or max(1, min(16, len(os.sched_getaffinity(0))))
-    shards = {r: wl.shard_table(w, r) for r in w.ranks}
+    if shards is None:
+        shards = {r: wl.shard_table(w, r) for r in w.ranks}
     # LM head: bounded sample of rows when the full product would take too long
     M = w.seqs if w.seqs else hidden_h.shape[0]
     flops_full = 2.0 * M * w.shard_rows * w.dim * len(w.ranks)

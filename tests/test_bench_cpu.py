@@ -28,7 +28,8 @@ def test_more_than_one_gpu_is_refused():
 def test_help_lists_the_options():
     out = _run("--help").stdout
     for opt in ("--steps", "--warmup", "--workload", "--argmax", "--lm-rows", "--load-shard",
-                "--timed-events", "--no-breakdown", "--library-gemm", "--copy-probe-mib"):
+                "--timed-events", "--no-breakdown", "--library-gemm", "--copy-probe-mib",
+                "--no-extra-workloads"):
         assert opt in out, opt
 
 
@@ -107,3 +108,36 @@ def test_traffic_key_follows_the_lm_head_configuration():
     assert k("qwen3_0p6b_tp1_prefill", "embed", 0, True) == "qwen3_0p6b_tp1_prefill"
     # a configuration whose counters were never recorded reports none
     assert bench.recorded_traffic(k("qwen3_0p6b_tp2_rank0", "lmhead", 3), "lmhead") is None
+
+
+def test_extra_configurations_cover_every_workload():
+    names = {n for n, _ in bench.EXTRA_RUNS}
+    assert names | {bench.DEFAULT_WORKLOAD} >= set(wl.WORKLOAD_ORDER) - {"tiny_v4096_d64_f32_tp2"}
+    assert ("qwen3_0p6b_tp2_rank0", 1) in bench.EXTRA_RUNS
+    assert ("qwen3_0p6b_tp2_rank0", 16) in bench.EXTRA_RUNS
+
+
+def test_extra_configurations_only_with_the_default_step():
+    import argparse
+    base = dict(no_extra_workloads=False, workload=bench.DEFAULT_WORKLOAD, lm_rows=0,
+                argmax=False, unfused_prefill=False, timed_events="dominant", no_breakdown=False,
+                library_gemm=False, copy_probe_mib=0)
+    assert bench.want_extra_runs(argparse.Namespace(**base))
+    for k, v in [("no_extra_workloads", True), ("workload", "qwen3_0p6b_tp1_prefill"),
+                 ("lm_rows", 8), ("argmax", True), ("unfused_prefill", True),
+                 ("timed_events", "none"), ("no_breakdown", True), ("library_gemm", True),
+                 ("copy_probe_mib", 256)]:
+        assert not bench.want_extra_runs(argparse.Namespace(**{**base, k: v})), k
+
+
+def test_kernel_bound_follows_the_ridge_point():
+    # [256, 75968] x 1024: 204 flop/B, under the 312.5 ridge -> HBM
+    w = wl.WORKLOADS["qwen3_0p6b_tp2_rank0"]
+    b = 256 * 1024 * 2 + 75968 * 1024 * 2 + 256 * 75968 * 2
+    assert bench.kernel_bound("lmhead", "bf16", b, 2 * 256 * 75968 * 1024) == "hbm"
+    # [1024, 75968] x 1024: 510 flop/B -> MFMA
+    b = 1024 * 1024 * 2 + 75968 * 1024 * 2 + 1024 * 75968 * 2
+    assert bench.kernel_bound("lmhead", "bf16", b, 2 * 1024 * 75968 * 1024) == "mfma"
+    assert bench.kernel_bound("embed", "bf16", 1e6, 0) == "hbm"
+    assert bench.kernel_bound("lmhead", "f32", 1.0, 1e9) == "hbm"
+    del w
