@@ -82,6 +82,8 @@ def _load():
         lib.orc_lmhead_f64.argtypes = [vp, i64, i64, vp, i64, ci, vp, i64, i64, ci]
         lib.orc_logit_f64.argtypes = [vp, i64, vp, ci, i64, i64]
         lib.orc_argmax_rows.argtypes = [vp, i64, i64, i64, vp, vp]
+        lib.orc_logsumexp_rows.argtypes = [vp, i64, i64, i64, vp]
+        lib.orc_logsumexp_rows.restype = ci
         lib.orc_load_shard.argtypes = [vp, i64, i64, ci, i32, i32, vp]
         lib.orc_load_shard.restype = ci
         lib.orc_argmax_rows.restype = ci
@@ -237,6 +239,16 @@ def argmax_rows(logits: np.ndarray):
     idx = np.empty(m, dtype=np.int64)
     _check(_load().orc_argmax_rows(_ptr(logits), m, n, n, _ptr(mx), _ptr(idx)), "argmax_rows")
     return mx, idx
+
+
+def logsumexp_rows(logits: np.ndarray) -> np.ndarray:
+    """log(sum_j exp(logits[m, j])) of every row of an fp64 [m, n] array (the
+    softmax normaliser of each row), in fp64."""
+    logits = np.ascontiguousarray(logits, dtype=np.float64)
+    m, n = logits.shape
+    out = np.empty(m, dtype=np.float64)
+    _check(_load().orc_logsumexp_rows(_ptr(logits), m, n, n, _ptr(out)), "logsumexp_rows")
+    return out
 
 
 def round_bf16(values) -> np.ndarray:

@@ -321,3 +321,30 @@ double orc_logit_f64(const void *x, int64_t dim, const void *weight, int dtype,
         acc += orc_elem_f64(x, dtype, m * dim + k) * orc_elem_f64(weight, dtype, j * dim + k);
     return acc;
 }
+
+/*
+ * Log-sum-exp of every row of fp64 logits: lse[m] = log(sum_j exp(z[m][j])),
+ * the normaliser of the softmax that turns the gathered logits into sampling
+ * probabilities ([Guide-3.3] section 6: compute_logits is kept apart from
+ * the forward so that the sampler can take the logits; [TP-vocab] section 4:
+ * the shard logits are gathered into the full vocabulary first).  Written
+ * with the row's largest logit factored out, lse = mx + log(sum_j
+ * exp(z[m][j] - mx)), which is the same number without overflow in exp.
+ * Columns are visited in increasing order.
+ */
+int orc_logsumexp_rows(const double *logits, int64_t m_rows, int64_t n_cols, int64_t ld,
+                       double *lse_out) {
+    if (m_rows < 0 || n_cols < 1 || ld < n_cols) return ORC_ERR_ARG;
+    if (m_rows == 0) return ORC_OK;
+    if (!logits || !lse_out) return ORC_ERR_ARG;
+    for (int64_t m = 0; m < m_rows; ++m) {
+        const double *row = logits + m * ld;
+        double mx = row[0];
+        for (int64_t j = 1; j < n_cols; ++j)
+            if (row[j] > mx) mx = row[j];
+        double sum = 0.0;
+        for (int64_t j = 0; j < n_cols; ++j) sum += exp(row[j] - mx);
+        lse_out[m] = mx + log(sum);
+    }
+    return ORC_OK;
+}

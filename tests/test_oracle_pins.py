@@ -7,6 +7,7 @@ invariants the pages state (the sum of masked partials is the full lookup;
 the concatenation of shard logits is the full product).
 """
 import json
+import math
 import os
 
 import numpy as np
@@ -380,3 +381,57 @@ def test_load_shard_rejects_uneven_split():
         oracle.load_shard(full, 3, 0)
     with pytest.raises(oracle.OracleError):
         oracle.load_shard(full, 2, 2)
+
+
+# ---------------------------------------------------------------------------
+# log-sum-exp of the logits rows (the softmax normaliser the sampler needs)
+# ---------------------------------------------------------------------------
+def test_logsumexp_closed_forms():
+    # n equal logits c: log(n e^c) = c + ln n  (a dropped or doubled term moves it by ln(1 +- 1/n))
+    for n in (1, 2, 3, 7, 1000, 151936):
+        for c in (0.0, -3.25, 17.5):
+            got = oracle.logsumexp_rows(np.full((1, n), c))[0]
+            assert abs(got - (c + math.log(n))) <= 1e-12 * max(1.0, abs(c) + math.log(n)), (n, c)
+    # one logit: the logit itself, exactly
+    assert oracle.logsumexp_rows(np.array([[-2.5]]))[0] == -2.5
+    # two logits a, b: max + log(1 + e^-|a-b|)
+    for a, b in [(0.0, 1.0), (5.0, -5.0), (-1e3, -1e3 + 2.0), (3.0, 3.0)]:
+        want = max(a, b) + math.log1p(math.exp(-abs(a - b)))
+        assert abs(oracle.logsumexp_rows(np.array([[a, b]]))[0] - want) <= 1e-12 * max(1, abs(want))
+
+
+def test_logsumexp_matches_library_routine():
+    from scipy.special import logsumexp
+    rng = np.random.default_rng(71)
+    for shape, scale in [((5, 1), 1.0), ((8, 333), 3.0), ((3, 151936), 2.0), ((4, 50), 300.0)]:
+        z = rng.standard_normal(shape) * scale
+        got = oracle.logsumexp_rows(z)
+        want = logsumexp(z, axis=1)
+        assert np.allclose(got, want, rtol=1e-12, atol=1e-12), shape
+
+
+def test_logsumexp_no_overflow_and_shift_invariance():
+    # logits past exp's range: the factored maximum keeps the value finite
+    z = np.array([[1000.0, 999.0, 998.0], [-1000.0, -1001.0, -1e4]])
+    got = oracle.logsumexp_rows(z)
+    assert np.all(np.isfinite(got))
+    assert abs(got[0] - (1000.0 + math.log(1 + math.exp(-1) + math.exp(-2)))) < 1e-12 * 1000
+    rng = np.random.default_rng(72)
+    z = rng.standard_normal((6, 200))
+    for c in (-50.0, 0.5, 123.0):
+        assert np.allclose(oracle.logsumexp_rows(z + c), oracle.logsumexp_rows(z) + c,
+                           rtol=0, atol=1e-12 * (1 + abs(c)))
+
+
+def test_logsumexp_of_concatenated_shards_combines_shard_values():
+    # the full row's value from its shards' values: log(sum_r exp(lse_r)),
+    # factored by the largest shard value (the combine across tp ranks)
+    rng = np.random.default_rng(73)
+    z = rng.standard_normal((5, 4 * 97)) * 4
+    full = oracle.logsumexp_rows(z)
+    parts = np.stack([oracle.logsumexp_rows(z[:, r * 97:(r + 1) * 97]) for r in range(4)], axis=1)
+    mx = parts.max(axis=1)
+    comb = mx + np.log(np.exp(parts - mx[:, None]).sum(axis=1))
+    assert np.allclose(full, comb, rtol=1e-12, atol=1e-12)
+    # and a shard's value never exceeds the full row's (every term is positive)
+    assert np.all(parts <= full[:, None] + 1e-12)
