@@ -52,7 +52,8 @@ typedef enum vpe_status {
     VPE_ERR_ALIGN = 4,  /* a pointer is not aligned to its element size */
     VPE_ERR_SHARD = 5,  /* tp split invalid: V % tp != 0, rank outside [0, tp) */
     VPE_ERR_LAUNCH = 6, /* the HIP runtime refused a kernel launch */
-    VPE_ERR_RANGE = 7   /* an output column range does not fit its row stride */
+    VPE_ERR_RANGE = 7,  /* an output column range does not fit its row stride */
+    VPE_ERR_WORKSPACE = 8 /* a workspace is smaller than the call needs */
 } vpe_status;
 
 typedef enum vpe_dtype {
@@ -298,6 +299,68 @@ vpe_status vpe_argmax_decode(const uint64_t *best, int64_t m, float *max_logit, 
  */
 vpe_status vpe_argmax_decode_clear(uint64_t *best, int64_t m, float *max_logit,
                                    int64_t *token, void *stream);
+
+/*
+ * Log-sum-exp of the logits rows, the normaliser of the softmax the sampler
+ * takes over the gathered logits ([Guide-3.3] section 6: compute_logits is
+ * kept apart so that the sampler can take the logits; [TP-vocab] section 4:
+ * each rank's shard of the logits is gathered into the full vocabulary
+ * first).  Split over vocabulary shards it needs no gather: each rank reduces
+ * its shard to one value per row,
+ *
+ *   shard_lse[i] = log(sum_j exp(z[i, j]))   over the shard's columns j,
+ *
+ * and the ranks combine those ([M] floats each) with
+ *
+ *   lse[i] = log(sum_r exp(shard_lse_r[i])).
+ *
+ * z is the logit as vpe_lmhead stores it: fp32 accumulation rounded to `dt`
+ * (round to nearest even), widened to fp32.  The exponentials, sums and
+ * logarithm are taken in fp32 with each set's largest logit factored out (no
+ * overflow for any finite logits), merged in a fixed order: results do not
+ * depend on timing.  Rows holding an infinite or NaN logit give an infinite
+ * or NaN value.
+ */
+
+/* Bytes of workspace vpe_lmhead_logsumexp needs at most for m rows of a
+ * shard of shard_rows rows (8 bytes per row per 64 shard rows).
+ * Host-only.  Errors: VPE_ERR_NULL, VPE_ERR_SHAPE (m < 0, shard_rows < 1,
+ * or a size past INT64_MAX). */
+vpe_status vpe_lmhead_logsumexp_workspace(int64_t m, int64_t shard_rows, int64_t *bytes);
+
+/*
+ * One shard's logits, as vpe_lmhead, and every row's shard_lse.
+ * x, m, dim, weight, shard_rows, dt: as vpe_lmhead.
+ * logits, ld_out, col_offset: as vpe_lmhead, or logits == NULL: nothing is
+ *          stored (ld_out and col_offset are then ignored).
+ * shard_lse  device float [m], written.
+ * workspace  device, at least vpe_lmhead_logsumexp_workspace(m, shard_rows)
+ *          bytes, 8-byte aligned; owned by the caller, needs no
+ *          initialisation, holds nothing the caller uses afterwards, and must
+ *          not be shared by calls that may run at the same time.
+ * m == 0 is a no-op.
+ * Errors: VPE_ERR_NULL, VPE_ERR_SHAPE (as vpe_lmhead_argmax), VPE_ERR_RANGE
+ * (logits given and its column range does not fit ld_out), VPE_ERR_DTYPE,
+ * VPE_ERR_ALIGN, VPE_ERR_WORKSPACE (workspace_bytes below the size above).
+ */
+vpe_status vpe_lmhead_logsumexp(const void *x, int64_t m, int64_t dim, const void *weight,
+                                int64_t shard_rows, vpe_dtype dt, void *logits, int64_t ld_out,
+                                int64_t col_offset, float *shard_lse, void *workspace,
+                                int64_t workspace_bytes, void *stream);
+
+/*
+ * The ranks' shard_lse values combined into the log-sum-exp of the full
+ * rows: lse[i] = log(sum_r exp(shard_lse[r][i])), r in shard order (the
+ * exchange step of the log-sum-exp, done on one device as vpe_sum_partials
+ * does the embedding's).
+ * shard_lse  HOST array of n_parts device pointers, each float [m].
+ * lse        device float [m]; may equal one of the inputs.
+ * m == 0 is a no-op.
+ * Errors: VPE_ERR_NULL, VPE_ERR_SHAPE (n_parts outside [1, VPE_MAX_PARTS],
+ * m < 0), VPE_ERR_ALIGN.
+ */
+vpe_status vpe_logsumexp_combine(const float *const *shard_lse, int32_t n_parts, int64_t m,
+                                 float *lse, void *stream);
 
 /* Static, NUL-terminated name of a status code ("VPE_OK", ...). */
 const char *vpe_status_string(vpe_status s);

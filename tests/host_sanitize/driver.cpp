@@ -224,8 +224,80 @@ static void check_load_paths() {
   EXPECT(!bf16_direct_loads_ok(0x1000, 0x2000, 1020, false, 0, 256, 320));
 }
 
+// The log-sum-exp entry points: the workspace bound (8 bytes per row per 64
+// shard rows, overflow refused), validation before any launch, and what the
+// launcher is asked for.
+static void check_logsumexp() {
+  const int64_t kMax = INT64_MAX;
+  int64_t bytes = -1;
+  EXPECT(vpe_lmhead_logsumexp_workspace(256, 75968, &bytes) == VPE_OK && bytes == 256 * 1187 * 8);
+  EXPECT(vpe_lmhead_logsumexp_workspace(1, 64, &bytes) == VPE_OK && bytes == 8);
+  EXPECT(vpe_lmhead_logsumexp_workspace(1, 65, &bytes) == VPE_OK && bytes == 16);
+  EXPECT(vpe_lmhead_logsumexp_workspace(0, 65, &bytes) == VPE_OK && bytes == 0);
+  EXPECT(vpe_lmhead_logsumexp_workspace(1 << 21, kMax, &bytes) == VPE_ERR_SHAPE);
+  EXPECT(vpe_lmhead_logsumexp_workspace(kMax, kMax, &bytes) == VPE_ERR_SHAPE);
+  EXPECT(vpe_lmhead_logsumexp_workspace(-1, 8, &bytes) == VPE_ERR_SHAPE);
+  EXPECT(vpe_lmhead_logsumexp_workspace(4, 0, &bytes) == VPE_ERR_SHAPE);
+  EXPECT(vpe_lmhead_logsumexp_workspace(4, 8, nullptr) == VPE_ERR_NULL);
+
+  float *lse = static_cast<float *>(fake(0x1000));
+  void *ws = fake(0x2000);
+  const int64_t need = 256 * 1187 * 8;
+  g_last = stub_call{};
+  EXPECT(vpe_lmhead_logsumexp(fake(), 256, 1024, fake(16), 75968, VPE_BF16, fake(32), 75968, 0,
+                              lse, ws, need, nullptr) == VPE_OK);
+  EXPECT(!strcmp(g_last.what, "lmhead_logsumexp") && g_last.lse == ws &&
+         g_last.lse_cap == need / 8 && g_last.shard_lse == lse && g_last.n0 == 256 &&
+         g_last.n1 == 75968 && g_last.n2 == 1024 && g_last.out == fake(32));
+  // no logits: nothing is stored, the stride and offset are ignored
+  EXPECT(vpe_lmhead_logsumexp(fake(), 256, 1024, fake(16), 75968, VPE_BF16, nullptr, -5, kMax, lse,
+                              ws, need, nullptr) == VPE_OK);
+  EXPECT(g_last.out == nullptr && g_last.n3 == 0);
+  g_last = stub_call{};
+  EXPECT(vpe_lmhead_logsumexp(fake(), 256, 1024, fake(16), 75968, VPE_BF16, fake(32), 75968, 0,
+                              lse, ws, need - 1, nullptr) == VPE_ERR_WORKSPACE);
+  EXPECT(g_last.what == nullptr);  // nothing launched
+  EXPECT(vpe_lmhead_logsumexp(fake(), 256, 1024, fake(16), 75968, VPE_BF16, fake(32), 75968, 0,
+                              lse, ws, -8, nullptr) == VPE_ERR_SHAPE);
+  EXPECT(vpe_lmhead_logsumexp(fake(), 256, 1024, fake(16), 75968, VPE_BF16, fake(32), 75968, 0,
+                              lse, nullptr, need, nullptr) == VPE_ERR_NULL);
+  EXPECT(vpe_lmhead_logsumexp(fake(), 256, 1024, fake(16), 75968, VPE_BF16, fake(32), 75968, 0,
+                              nullptr, ws, need, nullptr) == VPE_ERR_NULL);
+  EXPECT(vpe_lmhead_logsumexp(fake(), 256, 1024, fake(16), 75968, VPE_BF16, fake(32), 75968, 0,
+                              lse, fake(0x2004), need, nullptr) == VPE_ERR_ALIGN);
+  EXPECT(vpe_lmhead_logsumexp(fake(), 256, 1024, fake(16), 75968, VPE_BF16, fake(32), 75968, 1,
+                              lse, ws, need, nullptr) == VPE_ERR_RANGE);
+  EXPECT(vpe_lmhead_logsumexp(fake(), kMax, 1024, fake(16), 75968, VPE_BF16, fake(32), 75968, 0,
+                              lse, ws, kMax, nullptr) == VPE_ERR_SHAPE);
+  EXPECT(vpe_lmhead_logsumexp(fake(), 4, 8, fake(16), kMax, VPE_F32, nullptr, 0, 0, lse, ws, kMax,
+                              nullptr) == VPE_ERR_SHAPE);
+  EXPECT(vpe_lmhead_logsumexp(fake(), 0, 8, fake(16), 8, VPE_F32, nullptr, 0, 0, nullptr, nullptr,
+                              0, nullptr) == VPE_OK);
+  EXPECT(vpe_lmhead_logsumexp(fake(), 4, 8, fake(16), 8, (vpe_dtype)7, nullptr, 0, 0, lse, ws,
+                              64, nullptr) == VPE_ERR_DTYPE);
+
+  const float *parts[65];
+  for (int r = 0; r < 65; ++r) parts[r] = static_cast<const float *>(fake(0x4000 + 4096 * r));
+  g_last = stub_call{};
+  EXPECT(vpe_logsumexp_combine(parts, 3, 100, lse, nullptr) == VPE_OK);
+  EXPECT(!strcmp(g_last.what, "logsumexp_combine") && g_last.a == parts[0] &&
+         g_last.b == parts[2] && g_last.n0 == 100 && g_last.n1 == 3);
+  EXPECT(vpe_logsumexp_combine(parts, 64, 100, lse, nullptr) == VPE_OK);
+  EXPECT(vpe_logsumexp_combine(parts, 65, 100, lse, nullptr) == VPE_ERR_SHAPE);
+  EXPECT(vpe_logsumexp_combine(parts, 0, 100, lse, nullptr) == VPE_ERR_SHAPE);
+  EXPECT(vpe_logsumexp_combine(parts, 2, -1, lse, nullptr) == VPE_ERR_SHAPE);
+  EXPECT(vpe_logsumexp_combine(parts, 2, 0, nullptr, nullptr) == VPE_OK);
+  EXPECT(vpe_logsumexp_combine(nullptr, 2, 4, lse, nullptr) == VPE_ERR_NULL);
+  const float *with_null[2] = {parts[0], nullptr};
+  EXPECT(vpe_logsumexp_combine(with_null, 2, 4, lse, nullptr) == VPE_ERR_NULL);
+  const float *odd[2] = {parts[0], static_cast<const float *>(fake(0x4002))};
+  EXPECT(vpe_logsumexp_combine(odd, 2, 4, lse, nullptr) == VPE_ERR_ALIGN);
+  EXPECT(!strcmp(vpe_status_string(VPE_ERR_WORKSPACE), "VPE_ERR_WORKSPACE"));
+}
+
 int main() {
   check_load_paths();
+  check_logsumexp();
   check_abi();
   check_oracle();
   if (!g_fail) printf("host sanitizer driver: all expectations held\n");

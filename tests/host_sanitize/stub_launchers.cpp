@@ -30,11 +30,21 @@ int launch_sum_partials(const void *const *parts, int n_parts, int64_t n_elems, 
 
 int launch_lmhead(const void *x, int64_t m, int64_t k, const void *w, int64_t n, int dtype,
                   void *logits, int64_t ld, int64_t col_offset, void *, const int32_t *cu,
-                  int64_t n_tokens, uint64_t *best, int64_t id_base) {
-  g_last = stub_call{best ? (cu ? "lmhead_prefill_argmax" : "lmhead_argmax")
-                          : (cu ? "lmhead_prefill" : "lmhead"),
+                  int64_t n_tokens, uint64_t *best, int64_t id_base, float *lse_part,
+                  int64_t lse_cap, float *shard_lse) {
+  g_last = stub_call{lse_part ? "lmhead_logsumexp"
+                     : best   ? (cu ? "lmhead_prefill_argmax" : "lmhead_argmax")
+                              : (cu ? "lmhead_prefill" : "lmhead"),
                      x, w, best ? static_cast<void *>(best) : logits,
-                     m, n, k, best ? id_base : col_offset, dtype, cu ? n_tokens : ld};
+                     m, n, k, best ? id_base : col_offset, dtype, cu ? n_tokens : ld,
+                     lse_part, lse_cap, shard_lse};
+  return 0;
+}
+
+int launch_logsumexp_combine(const float *const *parts, int n_parts, int64_t m, float *lse,
+                             void *) {
+  g_last = stub_call{"logsumexp_combine", parts[0], parts[n_parts - 1], lse, m, n_parts, 0, 0, 0,
+                     0};
   return 0;
 }
 

@@ -10,6 +10,9 @@ struct stub_call {
   int64_t n0, n1, n2, n3;
   int i0;
   int64_t n4;
+  const void *lse = nullptr;  // log-sum-exp pairs buffer
+  int64_t lse_cap = 0;
+  const void *shard_lse = nullptr;
 };
 extern stub_call g_last;
 

@@ -28,7 +28,9 @@ def test_header_declares_the_calls():
                                   "vpe_argmax_init", "vpe_lmhead_argmax",
                                   "vpe_lmhead_prefill_argmax", "vpe_argmax_decode",
                                   "vpe_argmax_decode_clear",
-                                  "vpe_load_shard", "vpe_status_string"])
+                                  "vpe_load_shard", "vpe_lmhead_logsumexp_workspace",
+                                  "vpe_lmhead_logsumexp", "vpe_logsumexp_combine",
+                                  "vpe_status_string"])
 
 
 def test_library_exports_every_declared_symbol():

@@ -21,6 +21,7 @@ LIB_PATH = os.path.join(_PKG, "libvpe.so")
 
 VPE_OK, VPE_ERR_NULL, VPE_ERR_SHAPE, VPE_ERR_DTYPE = 0, 1, 2, 3
 VPE_ERR_ALIGN, VPE_ERR_SHARD, VPE_ERR_LAUNCH, VPE_ERR_RANGE = 4, 5, 6, 7
+VPE_ERR_WORKSPACE = 8
 VPE_F32, VPE_BF16 = 0, 1
 VPE_I32, VPE_I64 = 0, 1
 VPE_MAX_PARTS = 64
@@ -29,7 +30,8 @@ EXPORTED_SYMBOLS = ("vpe_shard_range", "vpe_embed", "vpe_sum_partials",
                     "vpe_last_token_select", "vpe_lmhead", "vpe_lmhead_prefill",
                     "vpe_argmax_init", "vpe_lmhead_argmax", "vpe_lmhead_prefill_argmax",
                     "vpe_argmax_decode", "vpe_argmax_decode_clear", "vpe_load_shard",
-                    "vpe_status_string")
+                    "vpe_lmhead_logsumexp_workspace", "vpe_lmhead_logsumexp",
+                    "vpe_logsumexp_combine", "vpe_status_string")
 
 
 class VpeError(RuntimeError):
@@ -92,6 +94,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.vpe_argmax_decode.argtypes = [vp, i64, vp, vp, vp]
     lib.vpe_argmax_decode_clear.argtypes = [vp, i64, vp, vp, vp]
     lib.vpe_load_shard.argtypes = [vp, i64, i64, ci, ctypes.c_int32, ctypes.c_int32, vp, vp]
+    lib.vpe_lmhead_logsumexp_workspace.argtypes = [i64, i64, ctypes.POINTER(i64)]
+    lib.vpe_lmhead_logsumexp.argtypes = [vp, i64, i64, vp, i64, ci, vp, i64, i64, vp, vp, i64, vp]
+    lib.vpe_logsumexp_combine.argtypes = [ctypes.POINTER(vp), i32, i64, vp, vp]
     for name in EXPORTED_SYMBOLS[:-1]:
         getattr(lib, name).restype = ci
     lib.vpe_status_string.argtypes = [ci]
@@ -390,12 +395,88 @@ def vpe_argmax_decode_clear(best):
     return _decode("vpe_argmax_decode_clear", best)
 
 
+def vpe_lmhead_logsumexp_workspace(m: int, shard_rows: int) -> int:
+    """Bytes of workspace vpe_lmhead_logsumexp needs at most for m rows of a shard."""
+    n = ctypes.c_int64()
+    _check("vpe_lmhead_logsumexp_workspace",
+           load_library().vpe_lmhead_logsumexp_workspace(m, shard_rows, ctypes.byref(n)))
+    return n.value
+
+
+def vpe_lmhead_logsumexp(x, weight, logits=None, col_offset: int = 0, shard_lse=None,
+                         workspace=None, store_logits: bool = True):
+    """One shard's logits (as vpe_lmhead, unless store_logits is False) and every
+    row's log-sum-exp over the shard's columns, shard_lse float32 [M].
+
+    Returns (logits or None, shard_lse).  `workspace` is a device tensor of at
+    least vpe_lmhead_logsumexp_workspace(M, R) bytes (allocated when None).
+    """
+    torch = _torch()
+    _need_device("x", x)
+    _need_device("weight", weight)
+    if x.dim() != 2 or weight.dim() != 2 or x.shape[1] != weight.shape[1]:
+        raise ValueError("x must be [m, dim] and weight [shard_rows, dim]")
+    if x.dtype != weight.dtype:
+        raise TypeError("x and weight must share a dtype")
+    m, d = x.shape
+    rows = weight.shape[0]
+    if store_logits:
+        if logits is None:
+            logits = torch.empty((m, col_offset + rows), dtype=x.dtype, device=x.device)
+        _need_device("logits", logits)
+        if logits.dim() != 2 or logits.shape[0] != m or logits.dtype != x.dtype:
+            raise ValueError("logits must be [m, ld] of x's dtype")
+        _same_device(x, logits)
+    elif logits is not None:
+        raise ValueError("logits given with store_logits=False")
+    if shard_lse is None:
+        shard_lse = torch.empty(m, dtype=torch.float32, device=x.device)
+    _need_device("shard_lse", shard_lse)
+    if shard_lse.dtype != torch.float32 or shard_lse.numel() != m:
+        raise ValueError("shard_lse must be a float32 tensor with one value per row of x")
+    need = vpe_lmhead_logsumexp_workspace(m, rows)
+    if workspace is None:
+        workspace = torch.empty(max(need, 8), dtype=torch.uint8, device=x.device)
+    _need_device("workspace", workspace)
+    _same_device(x, weight, shard_lse, workspace)
+    nbytes = workspace.numel() * workspace.element_size()
+    _check("vpe_lmhead_logsumexp", load_library().vpe_lmhead_logsumexp(
+        x.data_ptr(), m, d, weight.data_ptr(), rows, _dtype_code(x),
+        logits.data_ptr() if logits is not None else None,
+        logits.shape[1] if logits is not None else rows, int(col_offset), shard_lse.data_ptr(),
+        workspace.data_ptr(), nbytes, _stream_handle(x.device)))
+    return logits, shard_lse
+
+
+def vpe_logsumexp_combine(shard_lse: Sequence, out=None):
+    """log(sum_r exp(shard_lse[r])) per row: the ranks' values combined, in rank order."""
+    torch = _torch()
+    parts = list(shard_lse)
+    if not parts:
+        raise ValueError("need at least one shard's values")
+    for i, p in enumerate(parts):
+        _need_device(f"shard_lse[{i}]", p)
+        if p.dtype != torch.float32 or p.shape != parts[0].shape:
+            raise ValueError("shard values must be float32 tensors of one shape")
+    if out is None:
+        out = torch.empty_like(parts[0])
+    _need_device("out", out)
+    if out.dtype != torch.float32 or out.numel() != parts[0].numel():
+        raise ValueError("out must be float32 with one value per row")
+    _same_device(out, *parts)
+    arr = (ctypes.c_void_p * len(parts))(*[p.data_ptr() for p in parts])
+    _check("vpe_logsumexp_combine", load_library().vpe_logsumexp_combine(
+        arr, len(parts), parts[0].numel(), out.data_ptr(), _stream_handle(out.device)))
+    return out
+
+
 from .layers import ParallelLMHead, VocabParallelEmbedding  # noqa: E402
 
 __all__ = [
     "vpe_shard_range", "vpe_embed", "vpe_sum_partials", "vpe_last_token_select", "vpe_lmhead",
     "vpe_lmhead_prefill", "vpe_argmax_init", "vpe_lmhead_argmax", "vpe_lmhead_prefill_argmax",
     "vpe_argmax_decode", "vpe_argmax_decode_clear", "vpe_load_shard",
+    "vpe_lmhead_logsumexp_workspace", "vpe_lmhead_logsumexp", "vpe_logsumexp_combine",
     "VocabParallelEmbedding", "ParallelLMHead", "VpeError", "StaleLibraryError", "load_library",
     "check_library_current", "LIB_PATH",
 ]

@@ -62,10 +62,74 @@ constexpr int kBufferFlags = 0x00020000;
 // concatenated row picks).  Shards fold their candidates into one key per row
 // with an atomic max, so the combine across shards needs no extra step.
 // ---------------------------------------------------------------------------
-struct ArgmaxOut {
+struct TileOut {
   uint64_t *best;   // [M] keys, or nullptr: write logits instead
   int64_t id_base;  // vocabulary id of the shard's first row (vocab_start)
+  // Log-sum-exp partials, or nullptr: entry [row * lse_ld + tile] holds the
+  // pair (tile maximum, sum of exp(logit - maximum)) of that row over the
+  // columns of W tile `tile` (lse_ld = the number of W tiles, set by the
+  // launcher that picks the tile width)
+  float *lse;
+  int64_t lse_ld;
+  int64_t lse_cap;  // entries the partials buffer holds (checked by the launchers)
 };
+
+// ---------------------------------------------------------------------------
+// Log-sum-exp partials.  A row's log-sum-exp over a set of logits is kept as
+// the pair (m, s) = (largest logit, sum of exp(logit - m)); two disjoint sets
+// merge into (max(m1, m2), s1 exp(m1 - m) + s2 exp(m2 - m)).  An empty set is
+// (-inf, 0).  The logits are the stored values (fp32 accumulation rounded to
+// the logits dtype), so the value is the log-sum-exp of the logits a caller
+// reads back.  Merges happen in a fixed order, so results are reproducible.
+// ---------------------------------------------------------------------------
+// Maximum that keeps a NaN (fmaxf drops it): a row with a NaN logit must not
+// lose it before the sum.
+__device__ __forceinline__ float nan_max(float a, float b) { return (a != a || a > b) ? a : b; }
+
+__device__ __forceinline__ void lse_merge(float &m, float &s, float m2, float s2) {
+  const float mx = nan_max(m, m2);
+  // (-inf) - (-inf) would be NaN: an empty side contributes nothing
+  const float a = (m == -__builtin_huge_valf()) ? 0.f : s * __expf(m - mx);
+  const float b = (m2 == -__builtin_huge_valf()) ? 0.f : s2 * __expf(m2 - mx);
+  m = mx;
+  s = a + b;
+}
+
+// The stored value of an accumulated logit: rounded to bf16 and widened back.
+template <bool BF16>
+__device__ __forceinline__ float stored_logit(float v) {
+  if constexpr (BF16) return __uint_as_float(f32_to_bf16_bits(v) << 16);
+  return v;
+}
+
+// Per row of a wave's fragments (acc[i][j][r]: row mb + 16 j, column
+// nb + 16 i + r, nb the lane's first column), the pair over the tile's
+// columns below N, reduced over the 4 lanes that hold the same row.
+template <int FN, int FM, bool BF16>
+__device__ __forceinline__ void lse_rows(const f32x4 (&acc)[FN][FM], int64_t nb, int64_t N,
+                                         float (&mx)[FM], float (&sm)[FM]) {
+#pragma unroll
+  for (int j = 0; j < FM; ++j) {
+    float m = -__builtin_huge_valf();
+#pragma unroll
+    for (int i = 0; i < FN; ++i)
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        if (nb + i * 16 + r < N) m = nan_max(m, stored_logit<BF16>(acc[i][j][r]));
+    float s = 0.f;
+    if (m != -__builtin_huge_valf()) {
+#pragma unroll
+      for (int i = 0; i < FN; ++i)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          if (nb + i * 16 + r < N) s += __expf(stored_logit<BF16>(acc[i][j][r]) - m);
+    }
+    lse_merge(m, s, __shfl_xor(m, 16), __shfl_xor(s, 16));
+    lse_merge(m, s, __shfl_xor(m, 32), __shfl_xor(s, 32));
+    mx[j] = m;
+    sm[j] = s;
+  }
+}
 
 __device__ __forceinline__ uint64_t pick_key(float v, int64_t id) {
   const uint32_t u = __float_as_uint(v);
@@ -133,7 +197,7 @@ constexpr int kBig = kLoadMask;
 // ARGMAX folds each row's largest logit (rounded to bf16) into pick.best.
 template <int FN, int FM>
 __device__ __forceinline__ void argmax_keys(const f32x4 (&acc)[FN][FM], int64_t nb, bool full,
-                                            int64_t N, ArgmaxOut pick, uint64_t (&keys)[FM]) {
+                                            int64_t N, TileOut pick, uint64_t (&keys)[FM]) {
   {
     // The 4 lanes l, l^16, l^32, l^48 hold the same row m (16 columns each).
     // Wanted: the row's first largest logit as rounded to bf16, compared in
@@ -209,7 +273,7 @@ __device__ __forceinline__ void argmax_keys(const f32x4 (&acc)[FN][FM], int64_t 
 // hold the keys of rows mb + 16 j).
 template <int FM>
 __device__ __forceinline__ void argmax_fold(const uint64_t (&keys)[FM], int64_t mb, int64_t M,
-                                            ArgmaxOut pick) {
+                                            TileOut pick) {
 #pragma unroll
   for (int j = 0; j < FM; ++j)
     if ((threadIdx.x & 48) == 0 && mb + j * 16 < M)
@@ -221,7 +285,7 @@ template <int FN, int FM, bool ARGMAX>
 __device__ __forceinline__ void write_tile(const f32x4 (&acc)[FN][FM], int64_t nb, int64_t mb,
                                            bool full, int64_t M, int64_t N,
                                            uint16_t *__restrict__ out, int64_t ld,
-                                           int64_t col_off, ArgmaxOut pick) {
+                                           int64_t col_off, TileOut pick) {
   if constexpr (ARGMAX) {
     uint64_t keys[FM];
     argmax_keys<FN, FM>(acc, nb, full, N, pick, keys);
@@ -388,7 +452,7 @@ __global__ __launch_bounds__(C::NT) void lmhead_bf16_mfma(
     const uint16_t *__restrict__ X, int64_t M, int64_t K, const uint16_t *__restrict__ W,
     int64_t N, uint16_t *__restrict__ out, int64_t ld, int64_t col_off, int tiles_n,
     int tiles_m, int group_n, const int32_t *__restrict__ cu, int64_t n_tokens,
-    ArgmaxOut pick) {
+    TileOut pick) {
   // (device pass only: the host pass needs no more than the launch stub)
 #if defined(__HIP_DEVICE_COMPILE__)
   constexpr int BN = C::BN, BM = C::BM, WN = C::WN, WM = C::WM, BK = C::BK;
@@ -667,6 +731,51 @@ __global__ __launch_bounds__(C::NT) void lmhead_bf16_mfma(
   // the clamped loads past the last step may still be landing in LDS
   __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
   const bool full = n0 + BN <= N && m0 + BM <= M;
+  if constexpr (!ARGMAX) {
+    if (pick.lse != nullptr) {
+      // this W tile's log-sum-exp pair of every row; the WN waves that hold
+      // the same rows (different columns) merge theirs in LDS, in wave order
+      float mx[FM], sm[FM];
+      lse_rows<FN, FM, true>(acc, n0 + wn * TN + 4 * frag_grp, N, mx, sm);
+      if constexpr (WN > 1) {
+        float *pl = reinterpret_cast<float *>(lds_all);  // [WM][FM][16][WN] pairs
+        static_assert(WM * FM * 16 * WN * 8 <= kNumBuf * kBufElems * 2, "pairs fit the stages");
+        __syncthreads();  // every wave is done with the stages
+        if ((threadIdx.x & 48) == 0) {
+#pragma unroll
+          for (int j = 0; j < FM; ++j) {
+            float *e = pl + (((wm * FM + j) * 16 + frag_row) * WN + wn) * 2;
+            e[0] = mx[j];
+            e[1] = sm[j];
+          }
+        }
+        __syncthreads();
+        if (wn == 0) {
+#pragma unroll
+          for (int j = 0; j < FM; ++j) {
+            const float *e = pl + ((wm * FM + j) * 16 + frag_row) * WN * 2;
+            float m = e[0], sv = e[1];
+#pragma unroll
+            for (int w2 = 1; w2 < WN; ++w2) lse_merge(m, sv, e[2 * w2], e[2 * w2 + 1]);
+            mx[j] = m;
+            sm[j] = sv;
+          }
+        }
+      }
+      if (wn == 0 && (threadIdx.x & 48) == 0) {
+#pragma unroll
+        for (int j = 0; j < FM; ++j) {
+          const int64_t row = m0 + wm * TM + j * 16 + frag_row;
+          if (row < M) {
+            float *e = pick.lse + (row * pick.lse_ld + tn) * 2;
+            e[0] = mx[j];
+            e[1] = sm[j];
+          }
+        }
+      }
+    }
+    if (out == nullptr) return;  // log-sum-exp only: no logits stored
+  }
   if constexpr (!ARGMAX && (FM % 2 == 0) && kNumBuf * kBufElems >= NT / 64 * 32 * (TN + 8)) {
     if (full && ((ld | col_off) & 7) == 0 && (reinterpret_cast<uintptr_t>(out) & 15) == 0) {
       asm volatile("s_barrier" ::: "memory");  // every wave is done with the stages
@@ -770,7 +879,7 @@ __global__ __launch_bounds__(WV * 64) void lmhead_bf16_xreg(
     const uint16_t *__restrict__ X, int64_t M, int64_t K, const uint16_t *__restrict__ W,
     int64_t N, uint16_t *__restrict__ out, int64_t ld, int64_t col_off, int tiles_n,
     int tiles_m, int group_n, const int32_t *__restrict__ cu, int64_t n_tokens,
-    ArgmaxOut pick) {
+    TileOut pick) {
   // (device pass only: the host pass needs no more than the launch stub)
 #if defined(__HIP_DEVICE_COMPILE__)
   constexpr int BK = 64, KS = BK / 32;
@@ -901,6 +1010,25 @@ __global__ __launch_bounds__(WV * 64) void lmhead_bf16_xreg(
   // the clamped loads past the last step may still be landing
   __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
   const bool full = n0 + BN <= N && m0 + BM <= M;
+  if constexpr (!ARGMAX) {
+    if (pick.lse != nullptr) {
+      // a wave holds whole rows of the tile: its pairs are the tile's
+      float mx[FM], sm[FM];
+      lse_rows<FN, FM, true>(acc, n0 + 4 * frag_grp, N, mx, sm);
+      if ((threadIdx.x & 48) == 0) {
+#pragma unroll
+        for (int j = 0; j < FM; ++j) {
+          const int64_t row = m0 + wave * TM + j * 16 + frag_row;
+          if (row < M) {
+            float *e = pick.lse + (row * pick.lse_ld + tn) * 2;
+            e[0] = mx[j];
+            e[1] = sm[j];
+          }
+        }
+      }
+    }
+    if (out == nullptr) return;  // log-sum-exp only: no logits stored
+  }
   if constexpr (!ARGMAX && NS * BN * BK >= WV * 16 * (BN + 8)) {
     if (full && ((ld | col_off) & 7) == 0 && (reinterpret_cast<uintptr_t>(out) & 15) == 0) {
       asm volatile("s_barrier" ::: "memory");  // every wave is done with the stages
@@ -926,7 +1054,7 @@ __global__ __launch_bounds__(kBlock) void lmhead_f32_tiled(const float *__restri
                                                           int64_t N, float *__restrict__ out,
                                                           int64_t ld, int64_t col_off,
                                                           const int32_t *__restrict__ cu,
-                                                          int64_t n_tokens, ArgmaxOut pick) {
+                                                          int64_t n_tokens, TileOut pick) {
   constexpr int T = 64, TK = 16;
   __shared__ float sX[TK][T + 1];
   __shared__ float sW[TK][T + 1];
@@ -980,6 +1108,30 @@ __global__ __launch_bounds__(kBlock) void lmhead_f32_tiled(const float *__restri
     }
     return;
   }
+  if (pick.lse != nullptr) {
+    // the 16 threads with the same ty hold rows ty*4 + i: merge their pairs
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int64_t m = m0 + ty * 4 + i;
+      float mx = -__builtin_huge_valf(), sm = 0.f;
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        if (n0 + tx * 4 + j < N) mx = nan_max(mx, acc[i][j]);
+      if (mx != -__builtin_huge_valf()) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          if (n0 + tx * 4 + j < N) sm += __expf(acc[i][j] - mx);
+      }
+#pragma unroll
+      for (int d = 1; d < 16; d <<= 1) lse_merge(mx, sm, __shfl_xor(mx, d), __shfl_xor(sm, d));
+      if (tx == 0 && m < M) {
+        float *e = pick.lse + (m * pick.lse_ld + blockIdx.x) * 2;
+        e[0] = mx;
+        e[1] = sm;
+      }
+    }
+    if (out == nullptr) return;
+  }
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int64_t m = m0 + ty * 4 + i;
@@ -1014,13 +1166,50 @@ __global__ __launch_bounds__(kBlock) void argmax_decode_kernel(uint64_t *__restr
   if constexpr (CLEAR) best[i] = 0;
 }
 
+// One shard's log-sum-exp of every row from its W tiles' pairs (row-major
+// [m][tiles] pairs): one wave per row; lane l merges tiles l, l + 64, ... in
+// order, then the lanes merge in a fixed butterfly, so the result does not
+// depend on timing.
+__global__ __launch_bounds__(kBlock) void lse_tiles_kernel(const float *__restrict__ part,
+                                                          int tiles, int64_t m,
+                                                          float *__restrict__ shard_lse) {
+  const int64_t row = static_cast<int64_t>(blockIdx.x) * (kBlock / 64) + (threadIdx.x >> 6);
+  if (row >= m) return;  // (wave-uniform)
+  const int lane = threadIdx.x & 63;
+  const float *p = part + row * tiles * 2;
+  float mx = -__builtin_huge_valf(), sm = 0.f;
+  for (int t = lane; t < tiles; t += 64) lse_merge(mx, sm, p[2 * t], p[2 * t + 1]);
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) lse_merge(mx, sm, __shfl_xor(mx, d), __shfl_xor(sm, d));
+  if (lane == 0) shard_lse[row] = mx + logf(sm);  // (-inf for a row with no finite pair)
+}
+
+struct LseParts {
+  const float *p[64];
+};
+
+// The log-sum-exp of rows split over shards from the shards' values, merged
+// in shard order: lse = mx + log(sum_r exp(lse_r - mx)), mx = max_r lse_r.
+__global__ __launch_bounds__(kBlock) void lse_combine_kernel(LseParts parts, int n_parts,
+                                                            int64_t m, float *__restrict__ lse) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * kBlock + threadIdx.x;
+  if (i >= m) return;
+  float mx = -__builtin_huge_valf();
+  for (int r = 0; r < n_parts; ++r) mx = fmaxf(mx, parts.p[r][i]);
+  float sm = 0.f;
+  if (mx != -__builtin_huge_valf())
+    for (int r = 0; r < n_parts; ++r) sm += expf(parts.p[r][i] - mx);
+  lse[i] = mx == -__builtin_huge_valf() ? mx : mx + logf(sm);
+}
+
 template <class C>
 int launch_bf16_cfg(const uint16_t *x, int64_t m, int64_t k, const uint16_t *w, int64_t n,
-                    uint16_t *out, int64_t ld, int64_t col_off, hipStream_t st, int group_n = 1,
-                    const int32_t *cu = nullptr, int64_t n_tokens = 0,
-                    ArgmaxOut pick = ArgmaxOut{nullptr, 0}) {
+                    uint16_t *out, int64_t ld, int64_t col_off, hipStream_t st, int group_n,
+                    const int32_t *cu, int64_t n_tokens, TileOut &pick) {
   const int64_t tn64 = (n + C::BN - 1) / C::BN, tm64 = (m + C::BM - 1) / C::BM;
   if (tn64 * tm64 > INT32_MAX) return static_cast<int>(hipErrorInvalidValue);
+  pick.lse_ld = tn64;
+  if (pick.lse != nullptr && tn64 > pick.lse_cap / m) return kErrWorkspace;
   const int tiles_n = static_cast<int>(tn64);
   const int tiles_m = static_cast<int>(tm64);
   const dim3 grid(static_cast<unsigned>(tiles_n) * static_cast<unsigned>(tiles_m));
@@ -1057,7 +1246,7 @@ int launch_bf16_cfg(const uint16_t *x, int64_t m, int64_t k, const uint16_t *w, 
 template <int BN, int WV, int TM, int NS>
 bool launch_bf16_xreg(const uint16_t *x, int64_t m, int64_t k, const uint16_t *w, int64_t n,
                       uint16_t *out, int64_t ld, int64_t col_off, hipStream_t st, int group_n,
-                      const int32_t *cu, int64_t n_tokens, ArgmaxOut pick, int *rc) {
+                      const int32_t *cu, int64_t n_tokens, TileOut &pick, int *rc) {
   const bool gx = cu != nullptr;
   const bool vec = bf16_direct_loads_ok(reinterpret_cast<uint64_t>(x),
                                         reinterpret_cast<uint64_t>(w), k, gx, n_tokens, WV * TM,
@@ -1070,6 +1259,11 @@ bool launch_bf16_xreg(const uint16_t *x, int64_t m, int64_t k, const uint16_t *w
   }
   const int tiles_n = static_cast<int>(tn64), tiles_m = static_cast<int>(tm64);
   const dim3 grid(static_cast<unsigned>(tiles_n) * static_cast<unsigned>(tiles_m));
+  pick.lse_ld = tn64;
+  if (pick.lse != nullptr && tn64 > pick.lse_cap / m) {
+    *rc = kErrWorkspace;
+    return true;
+  }
 #define VPE_XREG(G, A)                                                                       \
   hipLaunchKernelGGL((lmhead_bf16_xreg<BN, WV, TM, NS, G, A>), grid, dim3(WV * 64), 0, st, x, m, \
                      k, w, n, out, ld, col_off, tiles_n, tiles_m, group_n, cu, n_tokens, pick)
@@ -1085,21 +1279,34 @@ bool launch_bf16_xreg(const uint16_t *x, int64_t m, int64_t k, const uint16_t *w
   return true;
 }
 
+// After an LM head whose tiles wrote log-sum-exp pairs (pick.lse), the merge
+// of each row's pairs into shard_lse.
+int finish_lse(const TileOut &pick, int64_t m, float *shard_lse, hipStream_t st) {
+  const int rc = static_cast<int>(hipGetLastError());
+  if (rc != 0 || pick.lse == nullptr) return rc;
+  const dim3 grid(static_cast<unsigned>((m + kBlock / 64 - 1) / (kBlock / 64)));
+  hipLaunchKernelGGL(lse_tiles_kernel, grid, dim3(kBlock), 0, st, pick.lse,
+                     static_cast<int>(pick.lse_ld), m, shard_lse);
+  return static_cast<int>(hipGetLastError());
+}
 
 }  // namespace
 
 int launch_lmhead(const void *x, int64_t m, int64_t k, const void *w, int64_t n, int dtype,
                   void *logits, int64_t ld, int64_t col_offset, void *stream,
-                  const int32_t *cu, int64_t n_tokens, uint64_t *best, int64_t id_base) {
-  const ArgmaxOut pick{best, id_base};
+                  const int32_t *cu, int64_t n_tokens, uint64_t *best, int64_t id_base,
+                  float *lse_part, int64_t lse_cap, float *shard_lse) {
+  TileOut pick{best, id_base, lse_part, 0, lse_cap};
   hipStream_t st = static_cast<hipStream_t>(stream);
   (void)hipGetLastError();  // clear a stale error so the status below is this launch's
   if (dtype == 0) {
     const dim3 grid(static_cast<unsigned>((n + 63) / 64), static_cast<unsigned>((m + 63) / 64));
+    pick.lse_ld = grid.x;
+    if (pick.lse != nullptr && pick.lse_ld > pick.lse_cap / m) return kErrWorkspace;
     hipLaunchKernelGGL(lmhead_f32_tiled, grid, dim3(kBlock), 0, st, static_cast<const float *>(x),
                        m, k, static_cast<const float *>(w), n, static_cast<float *>(logits), ld,
                        col_offset, cu, n_tokens, pick);
-    return static_cast<int>(hipGetLastError());
+    return finish_lse(pick, m, shard_lse, st);
   }
   const uint16_t *xb = static_cast<const uint16_t *>(x);
   const uint16_t *wb = static_cast<const uint16_t *>(w);
@@ -1173,6 +1380,17 @@ int launch_lmhead(const void *x, int64_t m, int64_t k, const void *w, int64_t n,
                                                        8, cu, n_tokens, pick, &rc))
     rc = launch_bf16_cfg<Cfg<320, 256, 2, 4, 64, 2>>(xb, m, k, wb, n, ob, ld, col_offset, st, 1, cu, n_tokens, pick);
   if (rc != 0) return rc;
+  return finish_lse(pick, m, shard_lse, st);
+}
+
+int launch_logsumexp_combine(const float *const *parts, int n_parts, int64_t m, float *lse,
+                             void *stream) {
+  (void)hipGetLastError();
+  LseParts pl{};
+  for (int r = 0; r < n_parts; ++r) pl.p[r] = parts[r];
+  const dim3 grid(static_cast<unsigned>((m + kBlock - 1) / kBlock));
+  hipLaunchKernelGGL(lse_combine_kernel, grid, dim3(kBlock), 0, static_cast<hipStream_t>(stream),
+                     pl, n_parts, m, lse);
   return static_cast<int>(hipGetLastError());
 }
 

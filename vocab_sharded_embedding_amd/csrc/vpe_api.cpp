@@ -19,7 +19,19 @@ bool aligned(const void *p, int64_t bytes) {
   return (reinterpret_cast<uintptr_t>(p) % static_cast<uintptr_t>(bytes)) == 0;
 }
 
-vpe_status launched(int rc) { return rc == 0 ? VPE_OK : VPE_ERR_LAUNCH; }
+vpe_status launched(int rc) {
+  if (rc == vpe::kErrWorkspace) return VPE_ERR_WORKSPACE;
+  return rc == 0 ? VPE_OK : VPE_ERR_LAUNCH;
+}
+
+// Largest number of log-sum-exp pairs one LM-head call writes: one per row
+// per W tile, tiles at least kMinTileRows rows wide (or -1 on overflow).
+int64_t lse_pairs_bound(int64_t m, int64_t shard_rows) {
+  // ceil(shard_rows / kMinTileRows) without forming shard_rows + kMinTileRows - 1
+  const int64_t tiles = shard_rows / vpe::kMinTileRows + (shard_rows % vpe::kMinTileRows != 0);
+  if (m > 0 && tiles > INT64_MAX / 8 / m) return -1;
+  return m * tiles;
+}
 
 // Largest element count any single tensor may have (far above what one
 // device holds): indexes inside the kernels are 64-bit and every grid stays
@@ -221,6 +233,56 @@ vpe_status vpe_argmax_decode_clear(uint64_t *best, int64_t m, float *max_logit, 
   return launched(vpe::launch_argmax_decode_clear(best, m, max_logit, token, stream));
 }
 
+vpe_status vpe_lmhead_logsumexp_workspace(int64_t m, int64_t shard_rows, int64_t *bytes) {
+  if (!bytes) return VPE_ERR_NULL;
+  if (m < 0 || shard_rows < 1) return VPE_ERR_SHAPE;
+  const int64_t pairs = lse_pairs_bound(m, shard_rows);
+  if (pairs < 0) return VPE_ERR_SHAPE;
+  *bytes = pairs * 8;
+  return VPE_OK;
+}
+
+vpe_status vpe_lmhead_logsumexp(const void *x, int64_t m, int64_t dim, const void *weight,
+                                int64_t shard_rows, vpe_dtype dt, void *logits, int64_t ld_out,
+                                int64_t col_offset, float *shard_lse, void *workspace,
+                                int64_t workspace_bytes, void *stream) {
+  if (!known_dtype(dt)) return VPE_ERR_DTYPE;
+  if (m < 0 || dim < 1 || shard_rows < 1) return VPE_ERR_SHAPE;
+  if (m > (int64_t(1) << 21) || dim > (int64_t(1) << 20) || shard_rows > kMaxElems / dim)
+    return VPE_ERR_SHAPE;
+  if (logits != nullptr) {
+    if (col_offset < 0 || ld_out < 1 || shard_rows > ld_out - col_offset) return VPE_ERR_RANGE;
+    if (m > kMaxElems / ld_out) return VPE_ERR_SHAPE;
+  }
+  if (workspace_bytes < 0) return VPE_ERR_SHAPE;
+  if (m == 0) return VPE_OK;
+  if (!x || !weight || !shard_lse || !workspace) return VPE_ERR_NULL;
+  if (!aligned(x, dtype_bytes(dt)) || !aligned(weight, dtype_bytes(dt)) ||
+      (logits && !aligned(logits, dtype_bytes(dt))) || !aligned(shard_lse, 4) ||
+      !aligned(workspace, 8))
+    return VPE_ERR_ALIGN;
+  const int64_t need = lse_pairs_bound(m, shard_rows);
+  if (need < 0 || workspace_bytes / 8 < need) return VPE_ERR_WORKSPACE;
+  return launched(vpe::launch_lmhead(x, m, dim, weight, shard_rows, dt == VPE_BF16 ? 1 : 0,
+                                     logits, logits ? ld_out : shard_rows,
+                                     logits ? col_offset : 0, stream, nullptr, 0, nullptr, 0,
+                                     static_cast<float *>(workspace), workspace_bytes / 8,
+                                     shard_lse));
+}
+
+vpe_status vpe_logsumexp_combine(const float *const *shard_lse, int32_t n_parts, int64_t m,
+                                 float *lse, void *stream) {
+  if (n_parts < 1 || n_parts > VPE_MAX_PARTS || m < 0 || m > kMaxElems) return VPE_ERR_SHAPE;
+  if (m == 0) return VPE_OK;
+  if (!shard_lse || !lse) return VPE_ERR_NULL;
+  for (int32_t r = 0; r < n_parts; ++r) {
+    if (!shard_lse[r]) return VPE_ERR_NULL;
+    if (!aligned(shard_lse[r], 4)) return VPE_ERR_ALIGN;
+  }
+  if (!aligned(lse, 4)) return VPE_ERR_ALIGN;
+  return launched(vpe::launch_logsumexp_combine(shard_lse, n_parts, m, lse, stream));
+}
+
 const char *vpe_status_string(vpe_status s) {
   switch (s) {
     case VPE_OK: return "VPE_OK";
@@ -231,6 +293,7 @@ const char *vpe_status_string(vpe_status s) {
     case VPE_ERR_SHARD: return "VPE_ERR_SHARD";
     case VPE_ERR_LAUNCH: return "VPE_ERR_LAUNCH";
     case VPE_ERR_RANGE: return "VPE_ERR_RANGE";
+    case VPE_ERR_WORKSPACE: return "VPE_ERR_WORKSPACE";
   }
   return "VPE_ERR_UNKNOWN";
 }

@@ -35,10 +35,29 @@ int launch_sum_partials(const void *const *parts, int n_parts, int64_t n_elems, 
 // With best != nullptr, no logits are stored: each row's largest logit (as
 // rounded to the dtype) and its id (id_base + column) are folded into the
 // 64-bit key best[i] by atomic max.
+// With lse_part != nullptr, every W tile also writes each row's log-sum-exp
+// pair (tile maximum, sum of exp(logit - maximum)) over its columns into
+// lse_part ([m][tiles] pairs of floats, at most lse_cap pairs), and a second
+// kernel merges them into shard_lse[i] = log(sum_j exp(logit[i, j])) over the
+// shard.  logits may then be nullptr (nothing stored).  Returns kErrWorkspace,
+// launching nothing, when the pairs would not fit lse_cap.
 int launch_lmhead(const void *x, int64_t m, int64_t k, const void *w, int64_t n, int dtype,
                   void *logits, int64_t ld, int64_t col_offset, void *stream,
                   const int32_t *cu = nullptr, int64_t n_tokens = 0, uint64_t *best = nullptr,
-                  int64_t id_base = 0);
+                  int64_t id_base = 0, float *lse_part = nullptr, int64_t lse_cap = 0,
+                  float *shard_lse = nullptr);
+
+// A launcher's status when a caller-sized buffer is too small for the launch
+// it chose (no HIP error code is negative).
+constexpr int kErrWorkspace = -1;
+
+// Narrowest W tile of any LM-head kernel: a launch writes at most
+// ceil(n / kMinTileRows) log-sum-exp pairs per row.
+constexpr int64_t kMinTileRows = 64;
+
+// lse[i] = log(sum_r exp(parts[r][i])) over n_parts <= 64 shards, in shard order.
+int launch_logsumexp_combine(const float *const *parts, int n_parts, int64_t m, float *lse,
+                             void *stream);
 
 // best[i] = 0 for i < m.
 int launch_argmax_init(uint64_t *best, int64_t m, void *stream);
