@@ -24,7 +24,9 @@
  * Conventions for every call:
  *   - Pointers named as device pointers must point to device memory (or memory
  *     the device can address) that the caller allocated and owns; the library
- *     allocates nothing, keeps no state between calls and never synchronises.
+ *     allocates nothing, keeps no state between calls and never synchronises
+ *     (vpe_lmhead_logsumexp_noalloc aside: it uses a static device array the
+ *     library holds per GPU, see there).
  *   - Tensors are dense and row-major unless a stride is given.
  *   - `stream` is a hipStream_t (NULL = the default stream). Work is enqueued
  *     on it and the call returns without waiting for it.
@@ -33,7 +35,8 @@
  *     which reports a launch the HIP runtime refused.
  *   - Values held in device memory (ids, cu_seqlens) are not validated: their
  *     out-of-range cases have defined results, stated per call.
- *   - Calls are thread-safe (no shared mutable state).
+ *   - Calls are thread-safe (no shared mutable state), except that calls of
+ *     vpe_lmhead_logsumexp_noalloc on one GPU share that GPU's static array.
  */
 #ifndef VPE_H
 #define VPE_H
@@ -347,6 +350,32 @@ vpe_status vpe_lmhead_logsumexp(const void *x, int64_t m, int64_t dim, const voi
                                 int64_t shard_rows, vpe_dtype dt, void *logits, int64_t ld_out,
                                 int64_t col_offset, float *shard_lse, void *workspace,
                                 int64_t workspace_bytes, void *stream);
+
+/* Bytes of the static device array vpe_lmhead_logsumexp_noalloc uses on each
+ * GPU (held from the first call on that GPU until the process ends). */
+#define VPE_NOALLOC_SCRATCH_BYTES (16 << 20)
+
+/*
+ * vpe_lmhead_logsumexp without a workspace, for callers that cannot allocate
+ * device memory: code under stream capture, tight serving loops, harnesses
+ * that forbid allocation.  The call allocates nothing: the tile pairs go to a
+ * static array of VPE_NOALLOC_SCRATCH_BYTES that the library holds on each
+ * GPU it runs on (the GPU of `stream`; the current one for the NULL stream).
+ * Arguments and results as vpe_lmhead_logsumexp, bit for bit.
+ * The array is shared by every call on that GPU and keeps nothing a call
+ * needs from an earlier one: calls on one GPU that may overlap in time (on
+ * different streams, or from several threads) race and must be ordered by the
+ * caller, e.g. on one stream.
+ * Errors: as vpe_lmhead_logsumexp (except those of the workspace arguments);
+ * VPE_ERR_WORKSPACE, with nothing enqueued, when the call needs more than
+ * VPE_NOALLOC_SCRATCH_BYTES (8 bytes per row per W tile: the chosen tiles
+ * are 64 to 320 shard rows wide, so m * shard_rows / 64 * 8 bytes always
+ * fits); VPE_ERR_LAUNCH also when the array's device address cannot be had.
+ */
+vpe_status vpe_lmhead_logsumexp_noalloc(const void *x, int64_t m, int64_t dim, const void *weight,
+                                        int64_t shard_rows, vpe_dtype dt, void *logits,
+                                        int64_t ld_out, int64_t col_offset, float *shard_lse,
+                                        void *stream);
 
 /*
  * The ranks' shard_lse values combined into the log-sum-exp of the full

@@ -293,6 +293,27 @@ static void check_logsumexp() {
   const float *odd[2] = {parts[0], static_cast<const float *>(fake(0x4002))};
   EXPECT(vpe_logsumexp_combine(odd, 2, 4, lse, nullptr) == VPE_ERR_ALIGN);
   EXPECT(!strcmp(vpe_status_string(VPE_ERR_WORKSPACE), "VPE_ERR_WORKSPACE"));
+
+  // the allocation-free variant: same validation, no workspace arguments
+  g_last = stub_call{};
+  EXPECT(vpe_lmhead_logsumexp_noalloc(fake(), 256, 1024, fake(16), 75968, VPE_BF16, fake(32),
+                                      75968, 0, lse, nullptr) == VPE_OK);
+  EXPECT(!strcmp(g_last.what, "lmhead_logsumexp_noalloc") && g_last.shard_lse == lse &&
+         g_last.n0 == 256 && g_last.n1 == 75968 && g_last.n2 == 1024 && g_last.out == fake(32));
+  EXPECT(vpe_lmhead_logsumexp_noalloc(fake(), 256, 1024, fake(16), 75968, VPE_BF16, nullptr, -1,
+                                      kMax, lse, nullptr) == VPE_OK);
+  EXPECT(g_last.out == nullptr && g_last.n3 == 0);
+  g_last = stub_call{};
+  EXPECT(vpe_lmhead_logsumexp_noalloc(fake(), 256, 1024, fake(16), 75968, VPE_BF16, fake(32),
+                                      75968, 1, lse, nullptr) == VPE_ERR_RANGE);
+  EXPECT(vpe_lmhead_logsumexp_noalloc(fake(), 256, 1024, fake(16), 75968, VPE_BF16, fake(32),
+                                      75968, 0, nullptr, nullptr) == VPE_ERR_NULL);
+  EXPECT(vpe_lmhead_logsumexp_noalloc(fake(), kMax, 1024, fake(16), 75968, VPE_BF16, nullptr, 0,
+                                      0, lse, nullptr) == VPE_ERR_SHAPE);
+  EXPECT(vpe_lmhead_logsumexp_noalloc(fake(), 4, 8, fake(16), 8, VPE_BF16, nullptr, 0, 0,
+                                      static_cast<float *>(fake(0x1002)), nullptr) ==
+         VPE_ERR_ALIGN);
+  EXPECT(g_last.what == nullptr);  // nothing launched by the rejected calls
 }
 
 int main() {

@@ -41,6 +41,14 @@ int launch_lmhead(const void *x, int64_t m, int64_t k, const void *w, int64_t n,
   return 0;
 }
 
+int launch_lmhead_logsumexp_noalloc(const void *x, int64_t m, int64_t k, const void *w,
+                                    int64_t n, int dtype, void *logits, int64_t ld,
+                                    int64_t col_offset, float *shard_lse, void *) {
+  g_last = stub_call{"lmhead_logsumexp_noalloc", x, w, logits, m, n, k, col_offset, dtype, ld,
+                     nullptr, 0, shard_lse};
+  return 0;
+}
+
 int launch_logsumexp_combine(const float *const *parts, int n_parts, int64_t m, float *lse,
                              void *) {
   g_last = stub_call{"logsumexp_combine", parts[0], parts[n_parts - 1], lse, m, n_parts, 0, 0, 0,

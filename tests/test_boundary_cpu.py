@@ -30,7 +30,7 @@ def test_header_declares_the_calls():
                                   "vpe_argmax_decode_clear",
                                   "vpe_load_shard", "vpe_lmhead_logsumexp_workspace",
                                   "vpe_lmhead_logsumexp", "vpe_logsumexp_combine",
-                                  "vpe_status_string"])
+                                  "vpe_lmhead_logsumexp_noalloc", "vpe_status_string"])
 
 
 def test_library_exports_every_declared_symbol():

@@ -22,6 +22,7 @@ LIB_PATH = os.path.join(_PKG, "libvpe.so")
 VPE_OK, VPE_ERR_NULL, VPE_ERR_SHAPE, VPE_ERR_DTYPE = 0, 1, 2, 3
 VPE_ERR_ALIGN, VPE_ERR_SHARD, VPE_ERR_LAUNCH, VPE_ERR_RANGE = 4, 5, 6, 7
 VPE_ERR_WORKSPACE = 8
+VPE_NOALLOC_SCRATCH_BYTES = 16 << 20
 VPE_F32, VPE_BF16 = 0, 1
 VPE_I32, VPE_I64 = 0, 1
 VPE_MAX_PARTS = 64
@@ -31,7 +32,8 @@ EXPORTED_SYMBOLS = ("vpe_shard_range", "vpe_embed", "vpe_sum_partials",
                     "vpe_argmax_init", "vpe_lmhead_argmax", "vpe_lmhead_prefill_argmax",
                     "vpe_argmax_decode", "vpe_argmax_decode_clear", "vpe_load_shard",
                     "vpe_lmhead_logsumexp_workspace", "vpe_lmhead_logsumexp",
-                    "vpe_logsumexp_combine", "vpe_status_string")
+                    "vpe_logsumexp_combine", "vpe_lmhead_logsumexp_noalloc",
+                    "vpe_status_string")
 
 
 class VpeError(RuntimeError):
@@ -97,6 +99,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.vpe_lmhead_logsumexp_workspace.argtypes = [i64, i64, ctypes.POINTER(i64)]
     lib.vpe_lmhead_logsumexp.argtypes = [vp, i64, i64, vp, i64, ci, vp, i64, i64, vp, vp, i64, vp]
     lib.vpe_logsumexp_combine.argtypes = [ctypes.POINTER(vp), i32, i64, vp, vp]
+    lib.vpe_lmhead_logsumexp_noalloc.argtypes = [vp, i64, i64, vp, i64, ci, vp, i64, i64, vp, vp]
     for name in EXPORTED_SYMBOLS[:-1]:
         getattr(lib, name).restype = ci
     lib.vpe_status_string.argtypes = [ci]
@@ -448,6 +451,35 @@ def vpe_lmhead_logsumexp(x, weight, logits=None, col_offset: int = 0, shard_lse=
     return logits, shard_lse
 
 
+def vpe_lmhead_logsumexp_noalloc(x, weight, shard_lse, logits=None, col_offset: int = 0):
+    """vpe_lmhead_logsumexp without a workspace: the library's static per-GPU
+    array holds the tile pairs, so the call allocates nothing (outputs are the
+    caller's: shard_lse float32 [M], and logits [M, ld] or None to store none).
+    Calls that may overlap on one GPU race on that array."""
+    torch = _torch()
+    _need_device("x", x)
+    _need_device("weight", weight)
+    _need_device("shard_lse", shard_lse)
+    if x.dim() != 2 or weight.dim() != 2 or x.shape[1] != weight.shape[1]:
+        raise ValueError("x must be [m, dim] and weight [shard_rows, dim]")
+    if x.dtype != weight.dtype:
+        raise TypeError("x and weight must share a dtype")
+    if shard_lse.dtype != torch.float32 or shard_lse.numel() != x.shape[0]:
+        raise ValueError("shard_lse must be a float32 tensor with one value per row of x")
+    if logits is not None:
+        _need_device("logits", logits)
+        if logits.dim() != 2 or logits.shape[0] != x.shape[0] or logits.dtype != x.dtype:
+            raise ValueError("logits must be [m, ld] of x's dtype")
+        _same_device(x, logits)
+    _same_device(x, weight, shard_lse)
+    _check("vpe_lmhead_logsumexp_noalloc", load_library().vpe_lmhead_logsumexp_noalloc(
+        x.data_ptr(), x.shape[0], x.shape[1], weight.data_ptr(), weight.shape[0], _dtype_code(x),
+        logits.data_ptr() if logits is not None else None,
+        logits.shape[1] if logits is not None else weight.shape[0], int(col_offset),
+        shard_lse.data_ptr(), _stream_handle(x.device)))
+    return logits, shard_lse
+
+
 def vpe_logsumexp_combine(shard_lse: Sequence, out=None):
     """log(sum_r exp(shard_lse[r])) per row: the ranks' values combined, in rank order."""
     torch = _torch()
@@ -477,6 +509,6 @@ __all__ = [
     "vpe_lmhead_prefill", "vpe_argmax_init", "vpe_lmhead_argmax", "vpe_lmhead_prefill_argmax",
     "vpe_argmax_decode", "vpe_argmax_decode_clear", "vpe_load_shard",
     "vpe_lmhead_logsumexp_workspace", "vpe_lmhead_logsumexp", "vpe_logsumexp_combine",
-    "VocabParallelEmbedding", "ParallelLMHead", "VpeError", "StaleLibraryError", "load_library",
+    "vpe_lmhead_logsumexp_noalloc", "VocabParallelEmbedding", "ParallelLMHead", "VpeError", "StaleLibraryError", "load_library",
     "check_library_current", "LIB_PATH",
 ]

@@ -31,6 +31,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "vpe_bounds.h"
 #include "vpe_launch.h"
 
@@ -1381,6 +1383,62 @@ int launch_lmhead(const void *x, int64_t m, int64_t k, const void *w, int64_t n,
     rc = launch_bf16_cfg<Cfg<320, 256, 2, 4, 64, 2>>(xb, m, k, wb, n, ob, ld, col_offset, st, 1, cu, n_tokens, pick);
   if (rc != 0) return rc;
   return finish_lse(pick, m, shard_lse, st);
+}
+
+// ---------------------------------------------------------------------------
+// Allocation-free log-sum-exp: the tile pairs go to a static device array the
+// library holds on every GPU it runs on, instead of a caller workspace.  Host
+// code never uses the array's name as an address: each device's address comes
+// from hipGetSymbolAddress, taken once per device with that device current.
+// ---------------------------------------------------------------------------
+static __device__ __align__(256) float scratch[kNoAllocScratchBytes / sizeof(float)];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::once_flag g_scratch_once[kMaxDevices];
+void *g_scratch_ptr[kMaxDevices];
+hipError_t g_scratch_err[kMaxDevices];
+
+// The device the stream's work runs on (the current device for the null
+// stream), and that device's address of `scratch`, resolved on first use.
+int scratch_for_stream(hipStream_t st, void **ptr) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return static_cast<int>(e);
+  if (st != nullptr) {
+    hipDevice_t sd = 0;
+    e = hipStreamGetDevice(st, &sd);
+    if (e != hipSuccess) return static_cast<int>(e);
+    dev = static_cast<int>(sd);
+  }
+  if (dev < 0 || dev >= kMaxDevices) return static_cast<int>(hipErrorInvalidDevice);
+  std::call_once(g_scratch_once[dev], [dev]() {
+    int cur = 0;
+    hipError_t err = hipGetDevice(&cur);
+    if (err == hipSuccess && cur != dev) err = hipSetDevice(dev);
+    void *p = nullptr;
+    if (err == hipSuccess) err = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (cur != dev) (void)hipSetDevice(cur);
+    g_scratch_ptr[dev] = err == hipSuccess ? p : nullptr;
+    g_scratch_err[dev] = err;
+  });
+  if (g_scratch_err[dev] != hipSuccess) return static_cast<int>(g_scratch_err[dev]);
+  *ptr = g_scratch_ptr[dev];
+  return 0;
+}
+
+}  // namespace
+
+int launch_lmhead_logsumexp_noalloc(const void *x, int64_t m, int64_t k, const void *w,
+                                    int64_t n, int dtype, void *logits, int64_t ld,
+                                    int64_t col_offset, float *shard_lse, void *stream) {
+  void *ptr = nullptr;
+  const int rc = scratch_for_stream(static_cast<hipStream_t>(stream), &ptr);
+  if (rc != 0) return rc;
+  return launch_lmhead(x, m, k, w, n, dtype, logits, ld, col_offset, stream, nullptr, 0, nullptr,
+                       0, static_cast<float *>(ptr),
+                       static_cast<int64_t>(kNoAllocScratchBytes / 8), shard_lse);
 }
 
 int launch_logsumexp_combine(const float *const *parts, int n_parts, int64_t m, float *lse,

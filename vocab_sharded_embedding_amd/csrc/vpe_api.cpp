@@ -270,6 +270,30 @@ vpe_status vpe_lmhead_logsumexp(const void *x, int64_t m, int64_t dim, const voi
                                      shard_lse));
 }
 
+vpe_status vpe_lmhead_logsumexp_noalloc(const void *x, int64_t m, int64_t dim, const void *weight,
+                                        int64_t shard_rows, vpe_dtype dt, void *logits,
+                                        int64_t ld_out, int64_t col_offset, float *shard_lse,
+                                        void *stream) {
+  if (!known_dtype(dt)) return VPE_ERR_DTYPE;
+  if (m < 0 || dim < 1 || shard_rows < 1) return VPE_ERR_SHAPE;
+  if (m > (int64_t(1) << 21) || dim > (int64_t(1) << 20) || shard_rows > kMaxElems / dim)
+    return VPE_ERR_SHAPE;
+  if (logits != nullptr) {
+    if (col_offset < 0 || ld_out < 1 || shard_rows > ld_out - col_offset) return VPE_ERR_RANGE;
+    if (m > kMaxElems / ld_out) return VPE_ERR_SHAPE;
+  }
+  if (m == 0) return VPE_OK;
+  if (!x || !weight || !shard_lse) return VPE_ERR_NULL;
+  if (!aligned(x, dtype_bytes(dt)) || !aligned(weight, dtype_bytes(dt)) ||
+      (logits && !aligned(logits, dtype_bytes(dt))) || !aligned(shard_lse, 4))
+    return VPE_ERR_ALIGN;
+  // the exact pair count depends on the tile width the launcher picks; it
+  // refuses (kErrWorkspace) before launching anything when the array is short
+  return launched(vpe::launch_lmhead_logsumexp_noalloc(
+      x, m, dim, weight, shard_rows, dt == VPE_BF16 ? 1 : 0, logits, logits ? ld_out : shard_rows,
+      logits ? col_offset : 0, shard_lse, stream));
+}
+
 vpe_status vpe_logsumexp_combine(const float *const *shard_lse, int32_t n_parts, int64_t m,
                                  float *lse, void *stream) {
   if (n_parts < 1 || n_parts > VPE_MAX_PARTS || m < 0 || m > kMaxElems) return VPE_ERR_SHAPE;

@@ -55,6 +55,17 @@ constexpr int kErrWorkspace = -1;
 // ceil(n / kMinTileRows) log-sum-exp pairs per row.
 constexpr int64_t kMinTileRows = 64;
 
+// Bytes of the static per-device array the allocation-free log-sum-exp uses
+// for its tile pairs (8 bytes per row per W tile).
+constexpr int64_t kNoAllocScratchBytes = int64_t(16) << 20;
+
+// launch_lmhead with lse_part = that array (at most kNoAllocScratchBytes / 8
+// pairs; kErrWorkspace beyond), on the device `stream` belongs to.  Allocates
+// nothing.  Calls that overlap on one device share the array and race.
+int launch_lmhead_logsumexp_noalloc(const void *x, int64_t m, int64_t k, const void *w,
+                                    int64_t n, int dtype, void *logits, int64_t ld,
+                                    int64_t col_offset, float *shard_lse, void *stream);
+
 // lse[i] = log(sum_r exp(parts[r][i])) over n_parts <= 64 shards, in shard order.
 int launch_logsumexp_combine(const float *const *parts, int n_parts, int64_t m, float *lse,
                              void *stream);
