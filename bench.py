@@ -64,6 +64,10 @@ def parse_args():
     p.add_argument("--argmax", action="store_true",
                    help="LM head reduced on the fly to each row's greedy pick (largest logit "
                         "and its id) instead of storing the logits")
+    p.add_argument("--logsumexp", action="store_true",
+                   help="LM head that also reduces every row to its log-sum-exp over the shard "
+                        "(vpe_lmhead_logsumexp, logits stored), and the ranks' values combined "
+                        "(vpe_logsumexp_combine) when several ranks run")
     p.add_argument("--lm-rows", type=int, default=0,
                    help="override the workload's LM-head rows M (decode batch size; "
                         "not for prefill workloads, whose M is the number of sequences)")
@@ -195,7 +199,7 @@ def traffic_key(workload: str, kind: str, lm_rows_override: int = 0,
     return workload
 
 
-def algorithmic_bytes(w, ids, ranks_owned, fused_prefill=False, argmax=False):
+def algorithmic_bytes(w, ids, ranks_owned, fused_prefill=False, argmax=False, logsumexp=False):
     """Bytes the method must move per step, by kernel kind."""
     s = w.elem_bytes
     D = w.dim
@@ -217,6 +221,13 @@ def algorithmic_bytes(w, ids, ranks_owned, fused_prefill=False, argmax=False):
         out["lmhead_argmax"] = [M * D * s + R * D * s + M * 8 for _ in w.ranks]
         out["argmax_decode"] = [M * (8 + 8 + 12)]
         flops = {"lmhead_argmax": [2 * M * R * D for _ in w.ranks]}
+    elif logsumexp:
+        # as the stored-logits LM head, plus each row's value (4 bytes); the
+        # tile pairs live in a workspace of a few MB and are not counted
+        out["lmhead_lse"] = [M * D * s + R * D * s + M * R * s + M * 4 for _ in w.ranks]
+        flops = {"lmhead_lse": [2 * M * R * D for _ in w.ranks]}
+        if len(w.ranks) > 1:
+            out["lse_combine"] = [(len(w.ranks) + 1) * M * 4]
     else:
         out["lmhead"] = [M * D * s + R * D * s + M * R * s for _ in w.ranks]
         flops = {"lmhead": [2 * M * R * D for _ in w.ranks]}
@@ -277,10 +288,16 @@ def main():
     if args.load_shard:
         return bench_load_shard(args, w, lib, dev, _uploader(torch, dev))
 
+    if args.logsumexp and (args.argmax or w.seqs):
+        print("bench.py: --logsumexp applies to decode workloads with stored logits", file=sys.stderr)
+        sys.exit(2)
     res = measure(args, w, lib, dev, argmax=args.argmax, unfused_prefill=args.unfused_prefill,
                   timed_events=args.timed_events, breakdown=not args.no_breakdown,
                   library_gemm=args.library_gemm, copy_probe_mib=args.copy_probe_mib,
-                  lm_override=args.lm_rows, with_cpu=not args.no_cpu_baseline)
+                  lm_override=args.lm_rows,
+                  # (the oracle baseline covers the plain step: not the log-sum-exp variant)
+                  with_cpu=not args.no_cpu_baseline and not args.logsumexp,
+                  logsumexp=args.logsumexp)
 
     extras = None
     if want_extra_runs(args):
@@ -309,7 +326,8 @@ def main():
                    "rotating_copies": res["copies"],
                    "prefill_select": ("fused" if res["fused_prefill"] else "separate")
                    if w.seqs else None,
-                   "lm_output": "argmax" if args.argmax else "logits",
+                   "lm_output": ("argmax" if args.argmax else
+                                 "logits+logsumexp" if args.logsumexp else "logits"),
                    "step_algorithmic_bytes": res["step_bytes"]},
         "roofline": res["roofline"],
         "cpu_baseline": res["cpu_baseline"],
@@ -327,6 +345,7 @@ def want_extra_runs(args) -> bool:
     (diagnostic and single-workload runs, e.g. under a profiler, skip them)."""
     return (not args.no_extra_workloads and args.workload == DEFAULT_WORKLOAD
             and not args.lm_rows and not args.argmax and not args.unfused_prefill
+            and not getattr(args, "logsumexp", False)
             and args.timed_events == "dominant" and not args.no_breakdown
             and not args.library_gemm and not args.copy_probe_mib)
 
@@ -369,7 +388,7 @@ def _uploader(torch, dev):
 
 
 def measure(args, w, lib, dev, *, argmax, unfused_prefill, timed_events, breakdown,
-            library_gemm, copy_probe_mib, lm_override, with_cpu):
+            library_gemm, copy_probe_mib, lm_override, with_cpu, logsumexp=False):
     """Times args.steps steps of workload w (after args.warmup untimed ones) and
     returns the step rate, the dominant kernel's roofline entry and a per-kernel
     breakdown (see the module docstring for what is timed how)."""
@@ -422,6 +441,11 @@ def measure(args, w, lib, dev, *, argmax, unfused_prefill, timed_events, breakdo
         else:
             d["logits"] = torch.empty((M, w.vocab if w.concat else w.shard_rows), dtype=tdt,
                                       device=dev)
+        if logsumexp:
+            ws_bytes = vpe.vpe_lmhead_logsumexp_workspace(M, w.shard_rows)
+            d["lse_ws"] = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+            d["shard_lse"] = [torch.empty(M, dtype=torch.float32, device=dev) for _ in w.ranks]
+            d["lse"] = torch.empty(M, dtype=torch.float32, device=dev)
         sets.append(d)
     del base
     torch.cuda.synchronize()
@@ -469,11 +493,23 @@ def measure(args, w, lib, dev, *, argmax, unfused_prefill, timed_events, breakdo
                              w.seqs, d["shards"][r].data_ptr(), w.shard_rows, dcode,
                              d["logits"].data_ptr(), d["logits"].shape[1],
                              w.rank_start(r) if w.concat else 0, sh)))
+            elif logsumexp:
+                i = list(w.ranks).index(r)
+                seq.append(("lmhead_lse", lib.vpe_lmhead_logsumexp,
+                            (d["x"].data_ptr(), M, w.dim, d["shards"][r].data_ptr(), w.shard_rows,
+                             dcode, d["logits"].data_ptr(), d["logits"].shape[1],
+                             w.rank_start(r) if w.concat else 0, d["shard_lse"][i].data_ptr(),
+                             d["lse_ws"].data_ptr(), d["lse_ws"].numel(), sh)))
             else:
                 seq.append(("lmhead", lib.vpe_lmhead,
                             (d["x"].data_ptr(), M, w.dim, d["shards"][r].data_ptr(), w.shard_rows,
                              dcode, d["logits"].data_ptr(), d["logits"].shape[1],
                              w.rank_start(r) if w.concat else 0, sh)))
+        if logsumexp and len(w.ranks) > 1:
+            larr = (ctypes.c_void_p * len(w.ranks))(*[t.data_ptr() for t in d["shard_lse"]])
+            d["_larr"] = larr
+            seq.append(("lse_combine", lib.vpe_logsumexp_combine,
+                        (larr, len(w.ranks), M, d["lse"].data_ptr(), sh)))
         if argmax:
             # the decode clears the keys it reads: the next step's folds need no init
             seq.append(("argmax_decode", lib.vpe_argmax_decode_clear,
@@ -481,7 +517,8 @@ def measure(args, w, lib, dev, *, argmax, unfused_prefill, timed_events, breakdo
                          d["pick_tok"].data_ptr(), sh)))
         calls.append(seq)
 
-    bytes_, flops_ = algorithmic_bytes(w, ids_h, owned, fused_prefill=fused, argmax=argmax)
+    bytes_, flops_ = algorithmic_bytes(w, ids_h, owned, fused_prefill=fused, argmax=argmax,
+                                       logsumexp=logsumexp)
     step_bytes = sum(sum(v) for v in bytes_.values())
     # dominant kernel: most algorithmic bytes per step
     dom = max(bytes_, key=lambda k: sum(bytes_[k]))

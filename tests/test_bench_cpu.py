@@ -29,7 +29,7 @@ def test_help_lists_the_options():
     out = _run("--help").stdout
     for opt in ("--steps", "--warmup", "--workload", "--argmax", "--lm-rows", "--load-shard",
                 "--timed-events", "--no-breakdown", "--library-gemm", "--copy-probe-mib",
-                "--no-extra-workloads"):
+                "--no-extra-workloads", "--logsumexp"):
         assert opt in out, opt
 
 
@@ -141,3 +141,14 @@ def test_kernel_bound_follows_the_ridge_point():
     assert bench.kernel_bound("embed", "bf16", 1e6, 0) == "hbm"
     assert bench.kernel_bound("lmhead", "f32", 1.0, 1e9) == "hbm"
     del w
+
+
+def test_logsumexp_step_bytes():
+    w = wl.WORKLOADS["qwen3_0p6b_tp2_all_ranks"]
+    ids = wl.workload_ids(w)
+    b, f = bench.algorithmic_bytes(w, ids, _owned(w, ids), logsumexp=True)
+    M, R, D, s = w.lm_rows, w.shard_rows, w.dim, 2
+    assert b["lmhead_lse"] == [M * D * s + R * D * s + M * R * s + M * 4] * 2
+    assert b["lse_combine"] == [3 * M * 4]
+    assert f["lmhead_lse"] == [2 * M * R * D] * 2
+    assert "lmhead" not in b
