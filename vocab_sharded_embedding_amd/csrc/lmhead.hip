@@ -104,31 +104,79 @@ __device__ __forceinline__ float stored_logit(float v) {
   return v;
 }
 
+// A logit's stored value, rounded to bf16 (nearest, ties to even) and widened
+// back, for finite and infinite inputs (a NaN is carried separately below).
+__device__ __forceinline__ float bf16_value(float v) {
+  const uint32_t u = __float_as_uint(v);
+  return __uint_as_float((u + 0x7fffu + ((u >> 16) & 1u)) & 0xffff0000u);
+}
+
 // Per row of a wave's fragments (acc[i][j][r]: row mb + 16 j, column
 // nb + 16 i + r, nb the lane's first column), the pair over the tile's
 // columns below N, reduced over the 4 lanes that hold the same row.
+//  - Rounding to nearest even is monotone, so the largest stored logit is the
+//    rounding of the largest accumulator: the maximum needs no rounding per
+//    element.  fma(v, 0, bad) turns `bad` into NaN on any infinite or NaN
+//    accumulator, and a NaN maximum makes the row's value NaN.
+//  - Each term is 2^((v - m) log2 e) on the exponent unit (v_exp_f32).
+//  - A tile wholly inside N (`full`) runs without per-column checks; otherwise
+//    columns at or past N are left out by selects (no branches).
 template <int FN, int FM, bool BF16>
 __device__ __forceinline__ void lse_rows(const f32x4 (&acc)[FN][FM], int64_t nb, int64_t N,
-                                         float (&mx)[FM], float (&sm)[FM]) {
+                                         bool full, float (&mx)[FM], float (&sm)[FM]) {
+  constexpr float kLog2e = 1.4426950408889634f;
+  // this lane's columns nb + c, c = 16 i + r, lie below N for c < lim
+  const int64_t left = N - nb;
+  const int lim = left < 0 ? 0 : (left < FN * 16 ? static_cast<int>(left) : FN * 16);
 #pragma unroll
   for (int j = 0; j < FM; ++j) {
-    float m = -__builtin_huge_valf();
-#pragma unroll
-    for (int i = 0; i < FN; ++i)
-#pragma unroll
-      for (int r = 0; r < 4; ++r)
-        if (nb + i * 16 + r < N) m = nan_max(m, stored_logit<BF16>(acc[i][j][r]));
-    float s = 0.f;
-    if (m != -__builtin_huge_valf()) {
+    float a = -__builtin_huge_valf(), bad = 0.f;
+    if (full) {
 #pragma unroll
       for (int i = 0; i < FN; ++i)
 #pragma unroll
-        for (int r = 0; r < 4; ++r)
-          if (nb + i * 16 + r < N) s += __expf(stored_logit<BF16>(acc[i][j][r]) - m);
+        for (int r = 0; r < 4; ++r) {
+          a = fmaxf(a, acc[i][j][r]);
+          bad = fmaf(acc[i][j][r], 0.f, bad);
+        }
+    } else {
+#pragma unroll
+      for (int i = 0; i < FN; ++i)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const bool ok = i * 16 + r < lim;
+          a = ok ? fmaxf(a, acc[i][j][r]) : a;
+          bad = ok ? fmaf(acc[i][j][r], 0.f, bad) : bad;
+        }
     }
-    lse_merge(m, s, __shfl_xor(m, 16), __shfl_xor(s, 16));
-    lse_merge(m, s, __shfl_xor(m, 32), __shfl_xor(s, 32));
-    mx[j] = m;
+    // (a is -inf only for a lane with no column below N, or all logits -inf)
+    const bool any = a != -__builtin_huge_valf();
+    const float m = any ? (BF16 ? bf16_value(a) : a) : a;
+    const float mb = any ? -m * kLog2e : 0.f;
+    float s = 0.f;
+    if (full) {
+#pragma unroll
+      for (int i = 0; i < FN; ++i)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float v = BF16 ? bf16_value(acc[i][j][r]) : acc[i][j][r];
+          s += __builtin_amdgcn_exp2f(fmaf(v, kLog2e, mb));
+        }
+    } else {
+#pragma unroll
+      for (int i = 0; i < FN; ++i)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float v = BF16 ? bf16_value(acc[i][j][r]) : acc[i][j][r];
+          const float e = __builtin_amdgcn_exp2f(fmaf(v, kLog2e, mb));
+          s += (i * 16 + r < lim) ? e : 0.f;
+        }
+    }
+    float m2 = m + bad;  // NaN when an accumulator was NaN or infinite
+    s = any ? s : 0.f;
+    lse_merge(m2, s, __shfl_xor(m2, 16), __shfl_xor(s, 16));
+    lse_merge(m2, s, __shfl_xor(m2, 32), __shfl_xor(s, 32));
+    mx[j] = m2;
     sm[j] = s;
   }
 }
@@ -738,7 +786,7 @@ __global__ __launch_bounds__(C::NT) void lmhead_bf16_mfma(
       // this W tile's log-sum-exp pair of every row; the WN waves that hold
       // the same rows (different columns) merge theirs in LDS, in wave order
       float mx[FM], sm[FM];
-      lse_rows<FN, FM, true>(acc, n0 + wn * TN + 4 * frag_grp, N, mx, sm);
+      lse_rows<FN, FM, true>(acc, n0 + wn * TN + 4 * frag_grp, N, full, mx, sm);
       if constexpr (WN > 1) {
         float *pl = reinterpret_cast<float *>(lds_all);  // [WM][FM][16][WN] pairs
         static_assert(WM * FM * 16 * WN * 8 <= kNumBuf * kBufElems * 2, "pairs fit the stages");
@@ -1016,7 +1064,7 @@ __global__ __launch_bounds__(WV * 64) void lmhead_bf16_xreg(
     if (pick.lse != nullptr) {
       // a wave holds whole rows of the tile: its pairs are the tile's
       float mx[FM], sm[FM];
-      lse_rows<FN, FM, true>(acc, n0 + 4 * frag_grp, N, mx, sm);
+      lse_rows<FN, FM, true>(acc, n0 + 4 * frag_grp, N, full, mx, sm);
       if ((threadIdx.x & 48) == 0) {
 #pragma unroll
         for (int j = 0; j < FM; ++j) {
@@ -1116,13 +1164,14 @@ __global__ __launch_bounds__(kBlock) void lmhead_f32_tiled(const float *__restri
     for (int i = 0; i < 4; ++i) {
       const int64_t m = m0 + ty * 4 + i;
       float mx = -__builtin_huge_valf(), sm = 0.f;
+      const int64_t left = N - (n0 + tx * 4);  // this thread's columns below N: j < left
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-        if (n0 + tx * 4 + j < N) mx = nan_max(mx, acc[i][j]);
-      if (mx != -__builtin_huge_valf()) {
+      for (int j = 0; j < 4; ++j) mx = (j < left) ? nan_max(mx, acc[i][j]) : mx;
+      const bool any = mx != -__builtin_huge_valf();
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-          if (n0 + tx * 4 + j < N) sm += __expf(acc[i][j] - mx);
+      for (int j = 0; j < 4; ++j) {
+        const float e = __expf(acc[i][j] - mx);
+        sm += (any && j < left) ? e : 0.f;
       }
 #pragma unroll
       for (int d = 1; d < 16; d <<= 1) lse_merge(mx, sm, __shfl_xor(mx, d), __shfl_xor(sm, d));
