@@ -408,6 +408,48 @@ def test_lmhead_prefill_ragged(dtype, seqs, dim, rows):
     assert np.all(g[:, :col] == -1536.0) and np.all(g[:, col + rows:] == -1536.0)
 
 
+@pytest.mark.parametrize("seqs,dim,rows,seq_len", [
+    (32, 1024, 151936, 2048),  # the prefill workload's shape, 4 MB between rows
+    (17, 520, 3000, 700),      # K past two 256-column chunks, the last one partial
+    (1, 72, 640, 50),          # K inside one chunk, not a multiple of 64
+    (32, 4096, 3001, 300),     # 16 chunks; ragged tile tail
+    (5, 256, 129, 9),          # exactly one chunk
+])
+def test_prefill_gathered_rows_equal_select_then_lmhead(seqs, dim, rows, seq_len):
+    # up to 32 gathered rows take the kernel that keeps X resident in LDS in
+    # chunks of 256 columns: logits and greedy-pick keys must equal those of
+    # the select followed by the LM head bit for bit, and the oracle's
+    cu = wl.cu_seqlens_ragged(240 + seqs, seqs, max(1, seq_len // 2), seq_len)
+    H = wl.hidden_states(241 + seqs, int(cu[-1]), dim, "bf16")
+    W = wl.table_rows(242 + seqs, rows, dim, "bf16", 0, rows, std=0.5)
+    _say(f"prefill gathered S={seqs} D={dim} R={rows} T={int(cu[-1])}")
+    H_d, cu_d, W_d = to_dev(H), to_dev(cu), to_dev(W)
+    ld, col = rows + 11, 3
+    fused = torch.full((seqs, ld), -1536.0, dtype=torch.bfloat16, device=dev())
+    vpe.vpe_lmhead_prefill(H_d, cu_d, W_d, fused, col_offset=col)
+    sel = vpe.vpe_last_token_select(H_d, cu_d)
+    plain = torch.full((seqs, ld), -1536.0, dtype=torch.bfloat16, device=dev())
+    vpe.vpe_lmhead(sel, W_d, plain, col_offset=col)
+    got = to_host(fused)
+    assert got.tobytes() == to_host(plain).tobytes()
+    ref = oracle.lmhead_f64(oracle.last_token_select(H, cu), W, nthreads=oracle_threads())
+    assert_logits_close(got[:, col:col + rows], ref, f"gathered prefill S={seqs} D={dim}")
+    g = as_f64(got)
+    assert np.all(g[:, :col] == -1536.0) and np.all(g[:, col + rows:] == -1536.0)
+    keys = []
+    for fn in ("fused", "plain"):
+        best = torch.empty(seqs, dtype=torch.int64, device=dev())
+        vpe.vpe_argmax_init(best)
+        if fn == "fused":
+            vpe.vpe_lmhead_prefill_argmax(H_d, cu_d, W_d, 7, best)
+        else:
+            vpe.vpe_lmhead_argmax(sel, W_d, 7, best)
+        keys.append(to_host(best))
+    assert np.array_equal(keys[0], keys[1])
+    _, tok = vpe.vpe_argmax_decode(torch.from_numpy(keys[0]).to(dev()))
+    assert np.array_equal(to_host(tok), np.argmax(g[:, col:col + rows], axis=1) + 7)
+
+
 def test_lmhead_prefill_out_of_range_sequence_gives_zero_logits():
     H = wl.hidden_states(210, 10, 64, "bf16")
     W = wl.table_rows(211, 50, 64, "bf16", 0, 50, std=0.5)

@@ -97,16 +97,9 @@ __device__ __forceinline__ void lse_merge(float &m, float &s, float m2, float s2
   s = a + b;
 }
 
-// The stored value of an accumulated logit: rounded to bf16 and widened back.
-template <bool BF16>
-__device__ __forceinline__ float stored_logit(float v) {
-  if constexpr (BF16) return __uint_as_float(f32_to_bf16_bits(v) << 16);
-  return v;
-}
-
 // A logit's stored value, rounded to bf16 (nearest, ties to even) and widened
 // back, for finite and infinite inputs (a NaN is carried separately below).
-__device__ __forceinline__ float bf16_value(float v) {
+[[maybe_unused]] __device__ __forceinline__ float bf16_value(float v) {
   const uint32_t u = __float_as_uint(v);
   return __uint_as_float((u + 0x7fffu + ((u >> 16) & 1u)) & 0xffff0000u);
 }
@@ -862,6 +855,207 @@ __global__ __launch_bounds__(C::NT) void lmhead_bf16_mfma(
 #endif
 }
 
+// ---------------------------------------------------------------------------
+// Prefill LM head over a few gathered rows with X resident in LDS.  The BM X
+// rows are the last positions of packed sequences, rows of the prefill
+// activations far apart (2048-token sequences put them 4 MB apart).  Staged
+// at every k step, as the kernel above does, each step of every workgroup
+// touches BM distinct pages; measured on MI355X that costs ~2-5 us at the
+// [32, 151936] shape against the same kernel on adjacent rows.  Here the X
+// rows are loaded into LDS KC columns at a time (one load per chunk instead
+// of one per k step) and only W streams through the NS stages.  At the chunk
+// boundary the next chunk is loaded after the step's barrier and waited for
+// (one drain of the pipeline per chunk).
+// Resident layout: row q holds its KC-column chunk as 16-byte pieces, piece p
+// at slot p ^ (q & 7), so the 8 lanes of a fragment read pass (8 rows, one
+// piece) hit 8 distinct bank groups.
+// Every output element accumulates its k steps in the same order as in
+// lmhead_bf16_mfma (64-wide steps of two 32-wide MFMAs), so the logits and
+// greedy-pick keys equal those of the select followed by the LM head, bit
+// for bit.  Requires 16-byte aligned operands, K % 8 == 0 and gathered rows
+// that fit one descriptor (checked by the launcher).
+// ---------------------------------------------------------------------------
+template <class C, int KC, bool ARGMAX>
+__global__ __launch_bounds__(C::NT) void lmhead_bf16_gxres(
+    const uint16_t *__restrict__ X, int64_t M, int64_t K, const uint16_t *__restrict__ W,
+    int64_t N, uint16_t *__restrict__ out, int64_t ld, int64_t col_off, int tiles_n,
+    int tiles_m, const int32_t *__restrict__ cu, int64_t n_tokens, TileOut pick) {
+  // (device pass only: the host pass needs no more than the launch stub)
+#if defined(__HIP_DEVICE_COMPILE__)
+  constexpr int BN = C::BN, BM = C::BM, WN = C::WN, WM = C::WM, BK = C::BK, NS = C::NS;
+  constexpr int NT = C::NT, NW = NT / 64;
+  constexpr int TN = BN / WN, TM = BM / WM;
+  constexpr int FN = TN / 16, FM = TM / 16;
+  static_assert(FN * 16 == TN && FM * 16 == TM, "wave tile must be a multiple of 16");
+  static_assert(BK == 64 && KC % BK == 0, "chunks of whole 64-wide k steps");
+  constexpr int kPieces = BK / 8, kRowsPerPass = NT / kPieces;
+  constexpr int kPPT = (BN + kRowsPerPass - 1) / kRowsPerPass;  // W loads per lane per step
+  constexpr int kBufElems = kPPT * kRowsPerPass * BK;
+  constexpr int kRowsPerWaveLoad = 64 / kPieces;
+  constexpr int KS = BK / 32, SPC = KC / BK;  // MFMA k steps per step; steps per chunk
+  constexpr int PX = KC / 8;                  // 16-byte pieces per resident row
+  static_assert(PX % 8 == 0 && (BM * PX) % (64 * NW) == 0, "whole chunk loads per wave");
+  constexpr int XL = BM * PX / 64 / NW;       // chunk loads per lane
+  static_assert((NS - 2) * kPPT <= 63 && kPPT <= 63, "outstanding loads fit the vmcnt counter");
+  __shared__ __attribute__((aligned(16))) uint16_t lds_all[NS * kBufElems + BM * KC];
+  uint16_t(*lds)[kBufElems] = reinterpret_cast<uint16_t(*)[kBufElems]>(lds_all);
+  uint16_t *xres = lds_all + NS * kBufElems;
+
+  int tn, tm;
+  tile_of_block(blockIdx.x, tiles_n, tiles_m, 1, tn, tm);
+  const int64_t n0 = static_cast<int64_t>(tn) * BN;
+  const int64_t m0 = static_cast<int64_t>(tm) * BM;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int wn = wave % WN, wm = wave / WN;
+  const int frag_row = lane & 15, frag_grp = lane >> 4;
+  const int wave_u = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6);
+  const int lrow = lane / kPieces, lslot = lane % kPieces;
+  const int nk = static_cast<int>((K + BK - 1) / BK);
+  const int k_i = static_cast<int>(K);
+  const int row_bytes = k_i * 2;
+  const int w_rows = static_cast<int>((N - n0 < BN) ? N - n0 : BN);
+  const int x_rows = static_cast<int>((M - m0 < BM) ? M - m0 : BM);
+  const __amdgpu_buffer_rsrc_t w_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t *>(W + n0 * K), 0, w_rows * row_bytes, kBufferFlags);
+  const __amdgpu_buffer_rsrc_t x_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t *>(X), 0, static_cast<int>(n_tokens * K * 2), kBufferFlags);
+  // W rows of this lane's loads (byte offsets, -1 past W)
+  int w_off[kPPT];
+#pragma unroll
+  for (int p = 0; p < kPPT; ++p) {
+    const int row = p * kRowsPerPass + wave_u * kRowsPerWaveLoad + lrow;
+    w_off[p] = row < w_rows ? row * row_bytes : -1;
+  }
+  // Chunk load t of this wave fills flat slots [64 q, 64 q + 64) of the
+  // resident rows, q = t NW + wave: this lane's row is (64 q + lane) / PX.
+  // Its sequence end is loaded first; the first use comes after stage 0's W
+  // loads are out.
+  int32_t cu_end[XL];
+#pragma unroll
+  for (int t = 0; t < XL; ++t) {
+    const int r = ((t * NW + wave_u) * 64 + lane) / PX;
+    cu_end[t] = r < x_rows ? cu[m0 + r + 1] : 0;
+  }
+  auto dma_w = [&](int step, int buf) {
+    const int k0 = (step < nk ? step : nk - 1) * BK;  // steps past the end reload the last
+    uint16_t *base = lds[buf];
+#pragma unroll
+    for (int p = 0; p < kPPT; ++p) {
+      const int row0 = p * kRowsPerPass + wave_u * kRowsPerWaveLoad;  // wave-uniform
+      if (BN % kRowsPerPass != 0 && row0 >= BN) continue;
+      const int piece = lslot ^ lds_swizzle<BK>(row0 + lrow);
+      const bool ok = w_off[p] >= 0 && k0 + piece * 8 < k_i;
+      // (non-temporal: each W row is read once)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          w_rsrc, (__attribute__((address_space(3))) void *)(base + row0 * BK), 16,
+          ok ? w_off[p] + piece * 16 : kBig, k0 * 2, 0, 2);
+    }
+  };
+  int x_off[XL];  // byte offset of this lane's gathered row, -1 for none
+  auto dma_x = [&](int c) {
+#pragma unroll
+    for (int t = 0; t < XL; ++t) {
+      const int q = t * NW + wave_u;
+      const int f = q * 64 + lane, r = f / PX;
+      const int piece = (f - r * PX) ^ (r & 7);
+      const bool ok = x_off[t] >= 0 && c * KC + piece * 8 < k_i;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          x_rsrc, (__attribute__((address_space(3))) void *)(xres + q * 512), 16,
+          ok ? x_off[t] + piece * 16 : kBig, c * KC * 2, 0, 0);
+    }
+  };
+  // W stage 0, then chunk 0 (its offsets wait on cu), then W stages 1..NS-2:
+  // the in-order vmcnt count at step 0 then covers the chunk too
+  dma_w(0, 0);
+#pragma unroll
+  for (int t = 0; t < XL; ++t) {
+    pin_vgpr(cu_end[t]);
+    const int r = ((t * NW + wave_u) * 64 + lane) / PX;
+    const int64_t tk = static_cast<int64_t>(cu_end[t]) - 1;
+    x_off[t] = (r < x_rows && static_cast<uint64_t>(tk) < static_cast<uint64_t>(n_tokens))
+                   ? static_cast<int>(tk * K * 2) : -1;
+  }
+  dma_x(0);
+#pragma unroll
+  for (int st = 1; st < NS - 1; ++st) dma_w(st, st);
+
+  f32x4 acc[FN][FM];
+#pragma unroll
+  for (int i = 0; i < FN; ++i)
+#pragma unroll
+    for (int j = 0; j < FM; ++j) acc[i][j] = f32x4(0.f);
+  int rd = 0, wr = NS - 1;
+  for (int kt = 0; kt < nk; ++kt) {
+    // this wave's loads of step kt have landed once at most the later NS-2
+    // steps' W loads are outstanding; the barrier extends that to all waves
+    // and closes every wave's reads of the buffers refilled below
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm((NS - 2) * kPPT));
+    asm volatile("s_barrier" ::: "memory");
+    if (kt > 0 && kt % SPC == 0) {
+      // every wave is past the previous chunk: load the next one and wait
+      // for it (only the W step issued after it may stay in flight)
+      dma_x(kt / SPC);
+      dma_w(kt + NS - 1, wr);
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(kPPT));
+      asm volatile("s_barrier" ::: "memory");
+    } else {
+      dma_w(kt + NS - 1, wr);
+    }
+    const uint16_t *cur = lds[rd];
+    const int xp0 = (kt % SPC) * (BK / 8);
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const int piece = ks * 4 + frag_grp;
+      bf16x8 fa[FN], fb[FM];
+#pragma unroll
+      for (int i = 0; i < FN; ++i)
+        fa[i] = *reinterpret_cast<const bf16x8 *>(
+            cur + lds_piece_offset<BK>(wn * TN + i * 16 + frag_row, piece));
+#pragma unroll
+      for (int j = 0; j < FM; ++j) {
+        const int q = wm * TM + j * 16 + frag_row;
+        fb[j] = *reinterpret_cast<const bf16x8 *>(xres + q * KC + (((xp0 + piece) ^ (q & 7)) << 3));
+      }
+#pragma unroll
+      for (int j = 0; j < FM; ++j)
+#pragma unroll
+        for (int i = 0; i < FN; ++i)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+    }
+    rd = (rd + 1 == NS) ? 0 : rd + 1;
+    wr = (wr + 1 == NS) ? 0 : wr + 1;
+  }
+  // the clamped loads past the last step may still be landing in LDS
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+  const bool full = n0 + BN <= N && m0 + BM <= M;
+  if constexpr (ARGMAX && WN > 1) {
+    // the WN waves that hold the same rows combine their keys in LDS first
+    uint64_t keys[FM];
+    argmax_keys<FN, FM>(acc, n0 + wn * TN + 4 * frag_grp, full, N, pick, keys);
+    uint64_t *kl = reinterpret_cast<uint64_t *>(lds_all);  // [WM][FM][16][WN]
+    static_assert(WM * FM * 16 * WN * 8 <= NS * kBufElems * 2, "key exchange fits the stages");
+    __syncthreads();  // every wave is done with the stages
+    if ((threadIdx.x & 48) == 0) {
+#pragma unroll
+      for (int j = 0; j < FM; ++j) kl[((wm * FM + j) * 16 + frag_row) * WN + wn] = keys[j];
+    }
+    __syncthreads();
+    if (wn == 0) {
+#pragma unroll
+      for (int j = 0; j < FM; ++j)
+#pragma unroll
+        for (int w2 = 1; w2 < WN; ++w2)
+          keys[j] = umax64(keys[j], kl[((wm * FM + j) * 16 + frag_row) * WN + w2]);
+      argmax_fold<FM>(keys, m0 + wm * TM + frag_row, M, pick);
+    }
+    return;
+  }
+  write_tile<FN, FM, ARGMAX>(acc, n0 + wn * TN + 4 * frag_grp, m0 + wm * TM + frag_row, full, M,
+                             N, out, ld, col_off, pick);
+#endif
+}
+
 // One step of W into an LDS stage: lane l of wave w fills, in pass p, LDS
 // slot l % 8 of tile row p * kRowsPerPass + 8 w + l / 8 with that row's piece
 // slot ^ f(row); w_off[p] is the row's byte offset (-1: no such row).
@@ -1330,6 +1524,33 @@ bool launch_bf16_xreg(const uint16_t *x, int64_t m, int64_t k, const uint16_t *w
   return true;
 }
 
+// The resident-X gathered kernel (see lmhead_bf16_gxres); false when its
+// operand requirements do not hold and the caller must take another kernel.
+template <class C, int KC>
+bool launch_bf16_gxres(const uint16_t *x, int64_t m, int64_t k, const uint16_t *w, int64_t n,
+                       uint16_t *out, int64_t ld, int64_t col_off, hipStream_t st,
+                       const int32_t *cu, int64_t n_tokens, TileOut &pick, int *rc) {
+  if (cu == nullptr || pick.lse != nullptr ||
+      !bf16_direct_loads_ok(reinterpret_cast<uint64_t>(x), reinterpret_cast<uint64_t>(w), k, true,
+                            n_tokens, C::BM, C::BN))
+    return false;
+  const int64_t tn64 = (n + C::BN - 1) / C::BN, tm64 = (m + C::BM - 1) / C::BM;
+  if (tn64 * tm64 > INT32_MAX) {
+    *rc = static_cast<int>(hipErrorInvalidValue);
+    return true;
+  }
+  const int tiles_n = static_cast<int>(tn64), tiles_m = static_cast<int>(tm64);
+  const dim3 grid(static_cast<unsigned>(tiles_n) * static_cast<unsigned>(tiles_m));
+  if (pick.best)
+    hipLaunchKernelGGL((lmhead_bf16_gxres<C, KC, true>), grid, dim3(C::NT), 0, st, x, m, k, w, n,
+                       out, ld, col_off, tiles_n, tiles_m, cu, n_tokens, pick);
+  else
+    hipLaunchKernelGGL((lmhead_bf16_gxres<C, KC, false>), grid, dim3(C::NT), 0, st, x, m, k, w, n,
+                       out, ld, col_off, tiles_n, tiles_m, cu, n_tokens, pick);
+  *rc = 0;
+  return true;
+}
+
 // After an LM head whose tiles wrote log-sum-exp pairs (pick.lse), the merge
 // of each row's pairs into shard_lse.
 int finish_lse(const TileOut &pick, int64_t m, float *shard_lse, hipStream_t st) {
@@ -1407,7 +1628,17 @@ int launch_lmhead(const void *x, int64_t m, int64_t k, const void *w, int64_t n,
   // 320 x 128 tiles (one workgroup per CU) when 256-row ones would spill past
   // one round and 320-row ones fit it (the 75968-row shard: 238 tiles)
   const bool one_round_320 = direct_ok && (n + 255) / 256 > 256 && (n + 319) / 320 <= 256;
-  if (m <= 16 && one_round_192)
+  // Prefill over at most 32 gathered rows (the last positions of packed
+  // sequences): X resident in LDS, 128 x 32 tiles, three W stages, 256-column
+  // chunks (80 KB of LDS with the stages: two workgroups per CU).  On the
+  // [32, 151936] prefill shape 58.1-58.3 against 60.3-60.7 us for the kernel
+  // that restages the gathered rows at every k step; 55.0 against 59.0 us at
+  // 16 rows; 73.1 against 75.5 us on 37984 x 4096.
+  if (cu != nullptr && m <= 32 &&
+      launch_bf16_gxres<Cfg<128, 32, 4, 1, 64, 3, true>, 256>(xb, m, k, wb, n, ob, ld, col_offset,
+                                                              st, cu, n_tokens, pick, &rc))
+    ;
+  else if (m <= 16 && one_round_192)
     rc = launch_bf16_cfg<Cfg<192, 16, 4, 1, 64, 2, true>>(xb, m, k, wb, n, ob, ld, col_offset, st, 1, cu, n_tokens, pick);
   else if (m <= 16)
     rc = launch_bf16_cfg<Cfg<64, 16, 4, 1, 128, 4, true>>(xb, m, k, wb, n, ob, ld, col_offset, st, 1, cu, n_tokens, pick);
