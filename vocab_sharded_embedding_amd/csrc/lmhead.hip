@@ -1630,7 +1630,7 @@ int launch_lmhead(const void *x, int64_t m, int64_t k, const void *w, int64_t n,
   const bool one_round_320 = direct_ok && (n + 255) / 256 > 256 && (n + 319) / 320 <= 256;
   // Prefill over at most 32 gathered rows (the last positions of packed
   // sequences): X resident in LDS, 128 x 32 tiles, three W stages, 256-column
-  // chunks (80 KB of LDS with the stages: two workgroups per CU).  On the
+  // chunks (64 KB of LDS with the stages: two workgroups per CU).  On the
   // [32, 151936] prefill shape 58.1-58.3 against 60.3-60.7 us for the kernel
   // that restages the gathered rows at every k step; 55.0 against 59.0 us at
   // 16 rows; 73.1 against 75.5 us on 37984 x 4096.
