@@ -200,7 +200,11 @@ def traffic_key(workload: str, kind: str, lm_rows_override: int = 0,
 
 
 def algorithmic_bytes(w, ids, ranks_owned, fused_prefill=False, argmax=False, logsumexp=False):
-    """Bytes the method must move per step, by kernel kind."""
+    """Bytes the method must move per step, by kernel kind: a lookup reads its
+    ids and owned rows and writes every output row; the sum reads each partial
+    and writes one; the select reads the sequence ends and copies the rows;
+    an LM head reads X and W once and writes (or, for the greedy pick and the
+    log-sum-exp without logits, reduces) the logits."""
     s = w.elem_bytes
     D = w.dim
     idb = ids.dtype.itemsize

@@ -34,7 +34,7 @@ CXX_FLAGS = ["-O2", "-fPIC", "-std=c++17", "-Wall", "-Wextra", "-I", INCLUDE, "-
 
 def source_files() -> List[str]:
     """Every file the library is built from: kernels, the C-ABI layer, the
-    internal headers, the public header and this build script."""
+    internal headers, the public header and build.py itself."""
     names = sorted(f for f in os.listdir(CSRC)
                    if f.endswith((".hip", ".cpp", ".h")))
     return [os.path.join(CSRC, f) for f in names] + [os.path.join(INCLUDE, "vpe.h"),
