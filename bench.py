@@ -66,7 +66,8 @@ def parse_args():
                         "and its id) instead of storing the logits")
     p.add_argument("--logsumexp", action="store_true",
                    help="LM head that also reduces every row to its log-sum-exp over the shard "
-                        "(vpe_lmhead_logsumexp, logits stored), and the ranks' values combined "
+                        "(vpe_lmhead_logsumexp, or vpe_lmhead_prefill_logsumexp for prefill "
+                        "workloads; logits stored), and the ranks' values combined "
                         "(vpe_logsumexp_combine) when several ranks run")
     p.add_argument("--lm-rows", type=int, default=0,
                    help="override the workload's LM-head rows M (decode batch size; "
@@ -292,8 +293,9 @@ def main():
     if args.load_shard:
         return bench_load_shard(args, w, lib, dev, _uploader(torch, dev))
 
-    if args.logsumexp and (args.argmax or w.seqs):
-        print("bench.py: --logsumexp applies to decode workloads with stored logits", file=sys.stderr)
+    if args.logsumexp and args.argmax:
+        print("bench.py: --logsumexp applies to the LM head with stored logits, not to --argmax",
+              file=sys.stderr)
         sys.exit(2)
     res = measure(args, w, lib, dev, argmax=args.argmax, unfused_prefill=args.unfused_prefill,
                   timed_events=args.timed_events, breakdown=not args.no_breakdown,
@@ -490,6 +492,15 @@ def measure(args, w, lib, dev, *, argmax, unfused_prefill, timed_events, breakdo
                 seq.append(("lmhead_argmax", lib.vpe_lmhead_argmax,
                             (d["x"].data_ptr(), M, w.dim, d["shards"][r].data_ptr(), w.shard_rows,
                              dcode, w.rank_start(r), d["best"].data_ptr(), sh)))
+            elif logsumexp and fused:
+                # the log-sum-exp LM head reads each sequence's last position itself
+                i = list(w.ranks).index(r)
+                seq.append(("lmhead_lse", lib.vpe_lmhead_prefill_logsumexp,
+                            (d["hidden"].data_ptr(), hidden_h.shape[0], w.dim, d["cu"].data_ptr(),
+                             w.seqs, d["shards"][r].data_ptr(), w.shard_rows, dcode,
+                             d["logits"].data_ptr(), d["logits"].shape[1],
+                             w.rank_start(r) if w.concat else 0, d["shard_lse"][i].data_ptr(),
+                             d["lse_ws"].data_ptr(), d["lse_ws"].numel(), sh)))
             elif fused:
                 # the LM head reads each sequence's last position itself
                 seq.append(("lmhead", lib.vpe_lmhead_prefill,

@@ -351,6 +351,32 @@ vpe_status vpe_lmhead_logsumexp(const void *x, int64_t m, int64_t dim, const voi
                                 int64_t col_offset, float *shard_lse, void *workspace,
                                 int64_t workspace_bytes, void *stream);
 
+/*
+ * vpe_lmhead_logsumexp over the last position of every packed sequence: the
+ * prefill select folded in as vpe_lmhead_prefill folds it ([Guide-3.3]
+ * section 6: in prefill only each sequence's last position is projected, and
+ * its logits go to the sampler; [TP-vocab] section 4 for the shard product).
+ * Row s of the logits (when stored) and shard_lse[s] are those of
+ * hidden[cu_seqlens[s+1]-1] . weight^T.
+ * hidden, n_tokens, dim, cu_seqlens, n_seqs: as vpe_lmhead_prefill (a
+ * sequence whose last index falls outside [0, n_tokens) gets a row of zero
+ * logits, nothing is read, and so shard_lse = log(shard_rows)).
+ * weight, shard_rows, dt, logits, ld_out, col_offset, shard_lse: as
+ * vpe_lmhead_logsumexp with m = n_seqs; workspace: at least
+ * vpe_lmhead_logsumexp_workspace(n_seqs, shard_rows) bytes, as there.
+ * n_seqs == 0 is a no-op.  Logits and values equal those of
+ * vpe_last_token_select followed by vpe_lmhead_logsumexp on the selected
+ * rows, bit for bit.
+ * Errors: VPE_ERR_NULL, VPE_ERR_SHAPE (as vpe_lmhead_prefill), VPE_ERR_RANGE,
+ * VPE_ERR_DTYPE, VPE_ERR_ALIGN, VPE_ERR_WORKSPACE.
+ */
+vpe_status vpe_lmhead_prefill_logsumexp(const void *hidden, int64_t n_tokens, int64_t dim,
+                                        const int32_t *cu_seqlens, int64_t n_seqs,
+                                        const void *weight, int64_t shard_rows, vpe_dtype dt,
+                                        void *logits, int64_t ld_out, int64_t col_offset,
+                                        float *shard_lse, void *workspace,
+                                        int64_t workspace_bytes, void *stream);
+
 /* Bytes of the static device array vpe_lmhead_logsumexp_noalloc uses on each
  * GPU (held from the first call on that GPU until the process ends). */
 #define VPE_NOALLOC_SCRATCH_BYTES (16 << 20)

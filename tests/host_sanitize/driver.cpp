@@ -276,6 +276,40 @@ static void check_logsumexp() {
   EXPECT(vpe_lmhead_logsumexp(fake(), 4, 8, fake(16), 8, (vpe_dtype)7, nullptr, 0, 0, lse, ws,
                               64, nullptr) == VPE_ERR_DTYPE);
 
+  // prefill: the last-position select folded in, the same workspace rule
+  const int32_t *cu = static_cast<const int32_t *>(fake(0x3000));
+  const int64_t need_p = 32 * 2374 * 8;  // 32 sequences over 151936 shard rows
+  g_last = stub_call{};
+  EXPECT(vpe_lmhead_prefill_logsumexp(fake(), 65536, 1024, cu, 32, fake(16), 151936, VPE_BF16,
+                                      fake(32), 151936, 0, lse, ws, need_p, nullptr) == VPE_OK);
+  EXPECT(!strcmp(g_last.what, "lmhead_prefill_logsumexp") && g_last.n0 == 32 &&
+         g_last.n1 == 151936 && g_last.n2 == 1024 && g_last.n4 == 65536 && g_last.lse == ws &&
+         g_last.lse_cap == need_p / 8 && g_last.shard_lse == lse && g_last.out == fake(32));
+  EXPECT(vpe_lmhead_prefill_logsumexp(fake(), 65536, 1024, cu, 32, fake(16), 151936, VPE_BF16,
+                                      nullptr, -1, kMax, lse, ws, need_p, nullptr) == VPE_OK);
+  EXPECT(g_last.out == nullptr && g_last.n3 == 0);
+  g_last = stub_call{};
+  EXPECT(vpe_lmhead_prefill_logsumexp(fake(), 65536, 1024, cu, 32, fake(16), 151936, VPE_BF16,
+                                      fake(32), 151936, 0, lse, ws, need_p - 1, nullptr) ==
+         VPE_ERR_WORKSPACE);
+  EXPECT(g_last.what == nullptr);
+  EXPECT(vpe_lmhead_prefill_logsumexp(fake(), 65536, 1024, nullptr, 32, fake(16), 151936, VPE_BF16,
+                                      fake(32), 151936, 0, lse, ws, need_p, nullptr) ==
+         VPE_ERR_NULL);
+  EXPECT(vpe_lmhead_prefill_logsumexp(fake(), 65536, 1024, static_cast<const int32_t *>(fake(0x3002)),
+                                      32, fake(16), 151936, VPE_BF16, fake(32), 151936, 0, lse, ws,
+                                      need_p, nullptr) == VPE_ERR_ALIGN);
+  EXPECT(vpe_lmhead_prefill_logsumexp(fake(), int64_t(INT32_MAX) + 1, 8, cu, 32, fake(16), 64,
+                                      VPE_BF16, nullptr, 0, 0, lse, ws, kMax, nullptr) ==
+         VPE_ERR_SHAPE);
+  EXPECT(vpe_lmhead_prefill_logsumexp(fake(), 65536, 1024, cu, 32, fake(16), 151936, VPE_BF16,
+                                      fake(32), 151936, 1, lse, ws, need_p, nullptr) ==
+         VPE_ERR_RANGE);
+  EXPECT(vpe_lmhead_prefill_logsumexp(fake(), kMax, 1024, cu, kMax, fake(16), 151936, VPE_BF16,
+                                      nullptr, 0, 0, lse, ws, kMax, nullptr) == VPE_ERR_SHAPE);
+  EXPECT(vpe_lmhead_prefill_logsumexp(nullptr, 0, 8, nullptr, 0, nullptr, 8, VPE_F32, nullptr, 0, 0,
+                                      nullptr, nullptr, 0, nullptr) == VPE_OK);
+
   const float *parts[65];
   for (int r = 0; r < 65; ++r) parts[r] = static_cast<const float *>(fake(0x4000 + 4096 * r));
   g_last = stub_call{};

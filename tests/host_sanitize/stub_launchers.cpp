@@ -32,7 +32,7 @@ int launch_lmhead(const void *x, int64_t m, int64_t k, const void *w, int64_t n,
                   void *logits, int64_t ld, int64_t col_offset, void *, const int32_t *cu,
                   int64_t n_tokens, uint64_t *best, int64_t id_base, float *lse_part,
                   int64_t lse_cap, float *shard_lse) {
-  g_last = stub_call{lse_part ? "lmhead_logsumexp"
+  g_last = stub_call{lse_part ? (cu ? "lmhead_prefill_logsumexp" : "lmhead_logsumexp")
                      : best   ? (cu ? "lmhead_prefill_argmax" : "lmhead_argmax")
                               : (cu ? "lmhead_prefill" : "lmhead"),
                      x, w, best ? static_cast<void *>(best) : logits,

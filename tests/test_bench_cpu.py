@@ -152,3 +152,15 @@ def test_logsumexp_step_bytes():
     assert b["lse_combine"] == [3 * M * 4]
     assert f["lmhead_lse"] == [2 * M * R * D] * 2
     assert "lmhead" not in b
+
+
+def test_prefill_logsumexp_step_bytes():
+    # fused: the log-sum-exp LM head reads the selected rows itself (no select)
+    w = wl.WORKLOADS["qwen3_0p6b_tp1_prefill"]
+    ids = wl.workload_ids(w)
+    b, f = bench.algorithmic_bytes(w, ids, _owned(w, ids), fused_prefill=True, logsumexp=True)
+    M, R, D, s = w.lm_rows, w.shard_rows, w.dim, 2
+    assert b["lmhead_lse"] == [M * D * s + R * D * s + M * R * s + M * 4]
+    assert "select" not in b and "lse_combine" not in b
+    b2, _ = bench.algorithmic_bytes(w, ids, _owned(w, ids), fused_prefill=False, logsumexp=True)
+    assert b2["select"] == [w.seqs * (4 + 2 * D * s)]

@@ -29,7 +29,8 @@ def test_header_declares_the_calls():
                                   "vpe_lmhead_prefill_argmax", "vpe_argmax_decode",
                                   "vpe_argmax_decode_clear",
                                   "vpe_load_shard", "vpe_lmhead_logsumexp_workspace",
-                                  "vpe_lmhead_logsumexp", "vpe_logsumexp_combine",
+                                  "vpe_lmhead_logsumexp", "vpe_lmhead_prefill_logsumexp",
+                                  "vpe_logsumexp_combine",
                                   "vpe_lmhead_logsumexp_noalloc", "vpe_status_string"])
 
 

@@ -211,3 +211,112 @@ def test_parallel_lmhead_layer_logsumexp():
     got = to_host(vpe.ParallelLMHead.combine_logsumexp(parts)).astype(np.float64)
     ref = oracle.logsumexp_rows(ref_logits)
     assert np.all(np.abs(got - ref) <= TIGHT * np.maximum(1, np.abs(ref)))
+
+
+# ---------------------------------------------------------------------------
+# prefill: the last position of every packed sequence, select folded in
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("dtype,seqs,dim,rows,seq_len", [
+    ("bf16", 32, 1024, 151936, 2048),  # the prefill workload's shape
+    ("bf16", 17, 520, 3000, 700),      # decode-size tiles, K not a multiple of 64
+    ("bf16", 64, 256, 2100, 40),       # 128-row decode tiles
+    ("bf16", 200, 128, 1000, 9),       # 320 x 256 tiles
+    ("bf16", 300, 64, 2100, 5),        # X in registers, gathered
+    ("f32", 9, 64, 700, 30),
+    ("f32", 70, 40, 300, 12),
+])
+def test_prefill_logsumexp_equals_select_then_logsumexp(dtype, seqs, dim, rows, seq_len):
+    cu = wl.cu_seqlens_ragged(500 + seqs, seqs, max(1, seq_len // 2), seq_len)
+    H = wl.hidden_states(501 + seqs, int(cu[-1]), dim, dtype)
+    W = wl.table_rows(502 + seqs, rows, dim, dtype, 0, rows, std=0.5)
+    print(f"prefill logsumexp {dtype} S={seqs} D={dim} R={rows} T={int(cu[-1])}", flush=True)
+    H_d, cu_d, W_d = to_dev(H), to_dev(cu), to_dev(W)
+    lg_f, lse_f = vpe.vpe_lmhead_prefill_logsumexp(H_d, cu_d, W_d)
+    sel = vpe.vpe_last_token_select(H_d, cu_d)
+    lg_p, lse_p = vpe.vpe_lmhead_logsumexp(sel, W_d)
+    _, lse_alone = vpe.vpe_lmhead_prefill_logsumexp(H_d, cu_d, W_d, store_logits=False)
+    torch.cuda.synchronize()
+    assert to_host(lg_f).tobytes() == to_host(lg_p).tobytes()
+    assert to_host(lse_f).tobytes() == to_host(lse_p).tobytes()
+    assert to_host(lse_alone).tobytes() == to_host(lse_f).tobytes()
+    from scipy.special import logsumexp
+    own = logsumexp(as_f64(to_host(lg_f)), axis=1)
+    got = to_host(lse_f).astype(np.float64)
+    assert np.all(np.abs(got - own) <= 1e-5 * np.maximum(1, np.abs(own)))
+
+
+def test_prefill_logsumexp_exact_on_integer_logits():
+    seqs, dim, rows = 40, 64, 3000
+    cu = wl.cu_seqlens_ragged(520, seqs, 1, 30)
+    rng = np.random.default_rng(521)
+    H = wl.f32_to_bf16_bits(rng.integers(-1, 2, size=(int(cu[-1]), dim)).astype(np.float32))
+    W = wl.f32_to_bf16_bits(rng.integers(-1, 2, size=(rows, dim)).astype(np.float32))
+    lg, lse = vpe.vpe_lmhead_prefill_logsumexp(to_dev(H), to_dev(cu), to_dev(W))
+    ref_logits = oracle.lmhead_f64(oracle.last_token_select(H, cu), W)
+    assert np.array_equal(as_f64(to_host(lg)), ref_logits)
+    ref = oracle.logsumexp_rows(ref_logits)
+    assert np.all(np.abs(to_host(lse) - ref) <= TIGHT * np.maximum(1, np.abs(ref)))
+
+
+def test_prefill_logsumexp_out_of_range_sequence():
+    # an empty first sequence and one ending past the tokens: zero logits, so
+    # the value is log(shard rows)
+    H = wl.hidden_states(530, 10, 64, "bf16")
+    W = wl.table_rows(531, 50, 64, "bf16", 0, 50, std=0.5)
+    cu = np.array([0, 0, 4, 10, 12], dtype=np.int32)
+    lg, lse = vpe.vpe_lmhead_prefill_logsumexp(to_dev(H), to_dev(cu), to_dev(W))
+    got, val = as_f64(to_host(lg)), to_host(lse).astype(np.float64)
+    assert np.all(got[0] == 0) and np.all(got[3] == 0)
+    assert abs(val[0] - np.log(50)) < 1e-5 and abs(val[3] - np.log(50)) < 1e-5
+    ref = oracle.logsumexp_rows(oracle.lmhead_f64(H[[3, 9]], W))
+    assert np.all(np.abs(val[1:3] - ref) <= 2.0 ** -8 * np.abs(got[1:3]).max(axis=1) + 1e-4)
+
+
+def test_prefill_logsumexp_workspace_too_small_is_refused():
+    cu = np.array([0, 3, 7], dtype=np.int32)
+    H = wl.hidden_states(540, 7, 64, "bf16")
+    W = wl.table_rows(541, 1000, 64, "bf16", 0, 1000)
+    need = vpe.vpe_lmhead_logsumexp_workspace(2, 1000)
+    small = torch.empty(need - 8, dtype=torch.uint8, device=dev())
+    with pytest.raises(vpe.VpeError) as e:
+        vpe.vpe_lmhead_prefill_logsumexp(to_dev(H), to_dev(cu), to_dev(W), workspace=small)
+    assert e.value.status == vpe.VPE_ERR_WORKSPACE
+
+
+def test_prefill_logsumexp_workload():
+    w = wl.WORKLOADS["qwen3_0p6b_tp1_prefill"]
+    hidden = wl.workload_hidden(w)
+    cu = wl.workload_cu_seqlens(w)
+    W = wl.shard_table(w, w.ranks[0])
+    print(f"prefill logsumexp workload: S={w.seqs} R={w.shard_rows} D={w.dim}", flush=True)
+    lg, lse = vpe.vpe_lmhead_prefill_logsumexp(to_dev(hidden), to_dev(cu), to_dev(W))
+    ref_logits = oracle.lmhead_f64(oracle.last_token_select(hidden, cu), W,
+                                   nthreads=oracle_threads())
+    got = to_host(lse).astype(np.float64)
+    ref = oracle.logsumexp_rows(ref_logits)
+    bound = 2.0 ** -8 * np.abs(ref_logits).max(axis=1) + 1e-4
+    assert np.all(np.abs(got - ref) <= bound)
+    from scipy.special import logsumexp
+    own = logsumexp(as_f64(to_host(lg)), axis=1)
+    assert np.all(np.abs(got - own) <= 1e-5 * np.maximum(1, np.abs(own)))
+
+
+def test_parallel_lmhead_layer_prefill_logsumexp():
+    V, D, tp = 512, 64, 2
+    cu = wl.cu_seqlens_ragged(550, 6, 1, 9)
+    rng = np.random.default_rng(551)
+    H = wl.f32_to_bf16_bits(rng.integers(-1, 2, size=(int(cu[-1]), D)).astype(np.float32))
+    Wf = wl.f32_to_bf16_bits(rng.integers(-1, 2, size=(V, D)).astype(np.float32))
+    full_d, H_d, cu_d = to_dev(Wf), to_dev(H), to_dev(cu)
+    logits = torch.empty((6, V), dtype=torch.bfloat16, device=dev())
+    parts = []
+    for r in range(tp):
+        head = vpe.ParallelLMHead(V, D, tp_size=tp, tp_rank=r, device=dev())
+        head.weight_loader(head.weight, full_d)
+        _, lse = head.logsumexp(H_d, logits=logits, cu_seqlens=cu_d)
+        parts.append(lse)
+    ref_logits = oracle.lmhead_f64(oracle.last_token_select(H, cu), Wf)
+    assert np.array_equal(as_f64(to_host(logits)), ref_logits)
+    got = to_host(vpe.ParallelLMHead.combine_logsumexp(parts)).astype(np.float64)
+    ref = oracle.logsumexp_rows(ref_logits)
+    assert np.all(np.abs(got - ref) <= TIGHT * np.maximum(1, np.abs(ref)))

@@ -32,8 +32,8 @@ EXPORTED_SYMBOLS = ("vpe_shard_range", "vpe_embed", "vpe_sum_partials",
                     "vpe_argmax_init", "vpe_lmhead_argmax", "vpe_lmhead_prefill_argmax",
                     "vpe_argmax_decode", "vpe_argmax_decode_clear", "vpe_load_shard",
                     "vpe_lmhead_logsumexp_workspace", "vpe_lmhead_logsumexp",
-                    "vpe_logsumexp_combine", "vpe_lmhead_logsumexp_noalloc",
-                    "vpe_status_string")
+                    "vpe_lmhead_prefill_logsumexp", "vpe_logsumexp_combine",
+                    "vpe_lmhead_logsumexp_noalloc", "vpe_status_string")
 
 
 class VpeError(RuntimeError):
@@ -98,6 +98,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.vpe_load_shard.argtypes = [vp, i64, i64, ci, ctypes.c_int32, ctypes.c_int32, vp, vp]
     lib.vpe_lmhead_logsumexp_workspace.argtypes = [i64, i64, ctypes.POINTER(i64)]
     lib.vpe_lmhead_logsumexp.argtypes = [vp, i64, i64, vp, i64, ci, vp, i64, i64, vp, vp, i64, vp]
+    lib.vpe_lmhead_prefill_logsumexp.argtypes = [vp, i64, i64, vp, i64, vp, i64, ci, vp, i64,
+                                                 i64, vp, vp, i64, vp]
     lib.vpe_logsumexp_combine.argtypes = [ctypes.POINTER(vp), i32, i64, vp, vp]
     lib.vpe_lmhead_logsumexp_noalloc.argtypes = [vp, i64, i64, vp, i64, ci, vp, i64, i64, vp, vp]
     for name in EXPORTED_SYMBOLS[:-1]:
@@ -451,6 +453,53 @@ def vpe_lmhead_logsumexp(x, weight, logits=None, col_offset: int = 0, shard_lse=
     return logits, shard_lse
 
 
+def vpe_lmhead_prefill_logsumexp(hidden, cu_seqlens, weight, logits=None, col_offset: int = 0,
+                                 shard_lse=None, workspace=None, store_logits: bool = True):
+    """vpe_lmhead_logsumexp over the last position of every packed sequence
+    (hidden [T, D], cu_seqlens int32 [S+1]): the logits of those rows, unless
+    store_logits is False, and each row's log-sum-exp over the shard's columns,
+    shard_lse float32 [S].  Returns (logits or None, shard_lse)."""
+    torch = _torch()
+    _need_device("hidden", hidden)
+    _need_device("cu_seqlens", cu_seqlens)
+    _need_device("weight", weight)
+    if hidden.dim() != 2 or weight.dim() != 2 or hidden.shape[1] != weight.shape[1]:
+        raise ValueError("hidden must be [n_tokens, dim] and weight [shard_rows, dim]")
+    if hidden.dtype != weight.dtype:
+        raise TypeError("hidden and weight must share a dtype")
+    if cu_seqlens.dtype != torch.int32 or cu_seqlens.dim() != 1 or cu_seqlens.numel() < 1:
+        raise ValueError("cu_seqlens must be a 1-D int32 tensor with at least one entry")
+    t, d = hidden.shape
+    s = cu_seqlens.numel() - 1
+    rows = weight.shape[0]
+    if store_logits:
+        if logits is None:
+            logits = torch.empty((s, col_offset + rows), dtype=hidden.dtype, device=hidden.device)
+        _need_device("logits", logits)
+        if logits.dim() != 2 or logits.shape[0] != s or logits.dtype != hidden.dtype:
+            raise ValueError("logits must be [n_seqs, ld] of hidden's dtype")
+        _same_device(hidden, logits)
+    elif logits is not None:
+        raise ValueError("logits given with store_logits=False")
+    if shard_lse is None:
+        shard_lse = torch.empty(s, dtype=torch.float32, device=hidden.device)
+    _need_device("shard_lse", shard_lse)
+    if shard_lse.dtype != torch.float32 or shard_lse.numel() != s:
+        raise ValueError("shard_lse must be a float32 tensor with one value per sequence")
+    need = vpe_lmhead_logsumexp_workspace(s, rows)
+    if workspace is None:
+        workspace = torch.empty(max(need, 8), dtype=torch.uint8, device=hidden.device)
+    _need_device("workspace", workspace)
+    _same_device(hidden, cu_seqlens, weight, shard_lse, workspace)
+    nbytes = workspace.numel() * workspace.element_size()
+    _check("vpe_lmhead_prefill_logsumexp", load_library().vpe_lmhead_prefill_logsumexp(
+        hidden.data_ptr(), t, d, cu_seqlens.data_ptr(), s, weight.data_ptr(), rows,
+        _dtype_code(hidden), logits.data_ptr() if logits is not None else None,
+        logits.shape[1] if logits is not None else rows, int(col_offset), shard_lse.data_ptr(),
+        workspace.data_ptr(), nbytes, _stream_handle(hidden.device)))
+    return logits, shard_lse
+
+
 def vpe_lmhead_logsumexp_noalloc(x, weight, shard_lse, logits=None, col_offset: int = 0):
     """vpe_lmhead_logsumexp without a workspace: the library's static per-GPU
     array holds the tile pairs, so the call allocates nothing (outputs are the
@@ -508,7 +557,8 @@ __all__ = [
     "vpe_shard_range", "vpe_embed", "vpe_sum_partials", "vpe_last_token_select", "vpe_lmhead",
     "vpe_lmhead_prefill", "vpe_argmax_init", "vpe_lmhead_argmax", "vpe_lmhead_prefill_argmax",
     "vpe_argmax_decode", "vpe_argmax_decode_clear", "vpe_load_shard",
-    "vpe_lmhead_logsumexp_workspace", "vpe_lmhead_logsumexp", "vpe_logsumexp_combine",
+    "vpe_lmhead_logsumexp_workspace", "vpe_lmhead_logsumexp", "vpe_lmhead_prefill_logsumexp",
+    "vpe_logsumexp_combine",
     "vpe_lmhead_logsumexp_noalloc", "VocabParallelEmbedding", "ParallelLMHead", "VpeError", "StaleLibraryError", "load_library",
     "check_library_current", "LIB_PATH",
 ]

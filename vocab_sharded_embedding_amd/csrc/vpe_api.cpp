@@ -270,6 +270,38 @@ vpe_status vpe_lmhead_logsumexp(const void *x, int64_t m, int64_t dim, const voi
                                      shard_lse));
 }
 
+vpe_status vpe_lmhead_prefill_logsumexp(const void *hidden, int64_t n_tokens, int64_t dim,
+                                        const int32_t *cu_seqlens, int64_t n_seqs,
+                                        const void *weight, int64_t shard_rows, vpe_dtype dt,
+                                        void *logits, int64_t ld_out, int64_t col_offset,
+                                        float *shard_lse, void *workspace,
+                                        int64_t workspace_bytes, void *stream) {
+  if (!known_dtype(dt)) return VPE_ERR_DTYPE;
+  if (n_tokens < 0 || n_seqs < 0 || dim < 1 || shard_rows < 1) return VPE_ERR_SHAPE;
+  if (n_tokens > INT32_MAX || n_tokens > kMaxElems / dim || shard_rows > kMaxElems / dim)
+    return VPE_ERR_SHAPE;
+  if (n_seqs > (int64_t(1) << 21) || dim > (int64_t(1) << 20)) return VPE_ERR_SHAPE;
+  if (logits != nullptr) {
+    if (col_offset < 0 || ld_out < 1 || shard_rows > ld_out - col_offset) return VPE_ERR_RANGE;
+    if (n_seqs > kMaxElems / ld_out) return VPE_ERR_SHAPE;
+  }
+  if (workspace_bytes < 0) return VPE_ERR_SHAPE;
+  if (n_seqs == 0) return VPE_OK;
+  if (!hidden || !cu_seqlens || !weight || !shard_lse || !workspace) return VPE_ERR_NULL;
+  if (!aligned(hidden, dtype_bytes(dt)) || !aligned(weight, dtype_bytes(dt)) ||
+      (logits && !aligned(logits, dtype_bytes(dt))) || !aligned(cu_seqlens, 4) ||
+      !aligned(shard_lse, 4) || !aligned(workspace, 8))
+    return VPE_ERR_ALIGN;
+  const int64_t need = lse_pairs_bound(n_seqs, shard_rows);
+  if (need < 0 || workspace_bytes / 8 < need) return VPE_ERR_WORKSPACE;
+  return launched(vpe::launch_lmhead(hidden, n_seqs, dim, weight, shard_rows,
+                                     dt == VPE_BF16 ? 1 : 0, logits,
+                                     logits ? ld_out : shard_rows, logits ? col_offset : 0,
+                                     stream, cu_seqlens, n_tokens, nullptr, 0,
+                                     static_cast<float *>(workspace), workspace_bytes / 8,
+                                     shard_lse));
+}
+
 vpe_status vpe_lmhead_logsumexp_noalloc(const void *x, int64_t m, int64_t dim, const void *weight,
                                         int64_t shard_rows, vpe_dtype dt, void *logits,
                                         int64_t ld_out, int64_t col_offset, float *shard_lse,

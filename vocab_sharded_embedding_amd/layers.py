@@ -18,8 +18,8 @@ from typing import Optional, Sequence
 import torch
 
 from . import (vpe_embed, vpe_lmhead, vpe_lmhead_argmax, vpe_lmhead_logsumexp, vpe_lmhead_prefill,
-               vpe_logsumexp_combine,
-               vpe_lmhead_prefill_argmax, vpe_load_shard, vpe_shard_range, vpe_sum_partials)
+               vpe_lmhead_prefill_argmax, vpe_lmhead_prefill_logsumexp, vpe_load_shard,
+               vpe_logsumexp_combine, vpe_shard_range, vpe_sum_partials)
 
 
 class VocabParallelEmbedding(torch.nn.Module):
@@ -116,16 +116,21 @@ class ParallelLMHead(VocabParallelEmbedding):
         return vpe_lmhead_argmax(hidden, self.weight, self.vocab_start_idx, best)
 
     def logsumexp(self, hidden: torch.Tensor, logits: Optional[torch.Tensor] = None,
-                  store_logits: bool = True):
+                  store_logits: bool = True, cu_seqlens: Optional[torch.Tensor] = None):
         """This rank's logits (into ``logits`` as ``forward`` places them, unless
         ``store_logits`` is False) and each row's log-sum-exp over this rank's
-        vocabulary columns; returns (logits or None, shard_lse).  The ranks'
-        values combine with ``ParallelLMHead.combine_logsumexp``."""
+        vocabulary columns; with ``cu_seqlens`` (prefill) the rows are the last
+        positions of the packed sequences.  Returns (logits or None,
+        shard_lse).  The ranks' values combine with
+        ``ParallelLMHead.combine_logsumexp``."""
         col = 0
         if logits is not None and logits.shape[1] == self.num_embeddings:
             col = self.vocab_start_idx
         elif logits is not None and logits.shape[1] != self.num_embeddings_per_partition:
             raise ValueError("logits must be [M, V/tp] (one shard) or [M, V] (all shards)")
+        if cu_seqlens is not None:
+            return vpe_lmhead_prefill_logsumexp(hidden, cu_seqlens, self.weight, logits,
+                                                col_offset=col, store_logits=store_logits)
         return vpe_lmhead_logsumexp(hidden, self.weight, logits, col_offset=col,
                                     store_logits=store_logits)
 
