@@ -97,11 +97,12 @@ __device__ __forceinline__ void lse_merge(float &m, float &s, float m2, float s2
   s = a + b;
 }
 
-// A logit's stored value, rounded to bf16 (nearest, ties to even) and widened
-// back, for finite and infinite inputs (a NaN is carried separately below).
-[[maybe_unused]] __device__ __forceinline__ float bf16_value(float v) {
-  const uint32_t u = __float_as_uint(v);
-  return __uint_as_float((u + 0x7fffu + ((u >> 16) & 1u)) & 0xffff0000u);
+// Two logits' stored values: each rounded to bf16 (nearest, ties to even, one
+// v_cvt_pk_bf16_f32 for the pair) and widened back.
+__device__ __forceinline__ void bf16_values(float &a, float &b) {
+  const __bf16 x = static_cast<__bf16>(a), y = static_cast<__bf16>(b);
+  a = static_cast<float>(x);
+  b = static_cast<float>(y);
 }
 
 // Per row of a wave's fragments (acc[i][j][r]: row mb + 16 j, column
@@ -109,9 +110,10 @@ __device__ __forceinline__ void lse_merge(float &m, float &s, float m2, float s2
 // columns below N, reduced over the 4 lanes that hold the same row.
 //  - Rounding to nearest even is monotone, so the largest stored logit is the
 //    rounding of the largest accumulator: the maximum needs no rounding per
-//    element.  fma(v, 0, bad) turns `bad` into NaN on any infinite or NaN
-//    accumulator, and a NaN maximum makes the row's value NaN.
-//  - Each term is 2^((v - m) log2 e) on the exponent unit (v_exp_f32).
+//    element.
+//  - Each term is 2^((v - m) log2 e) on the exponent unit (v_exp_f32), v the
+//    stored logit.  A NaN logit, or an infinite one (inf - inf), makes the
+//    sum NaN, and a NaN sum makes the pair (NaN, NaN): no per-element test.
 //  - A tile wholly inside N (`full`) runs without per-column checks; otherwise
 //    columns at or past N are left out by selects (no branches).
 template <int FN, int FM, bool BF16>
@@ -123,50 +125,42 @@ __device__ __forceinline__ void lse_rows(const f32x4 (&acc)[FN][FM], int64_t nb,
   const int lim = left < 0 ? 0 : (left < FN * 16 ? static_cast<int>(left) : FN * 16);
 #pragma unroll
   for (int j = 0; j < FM; ++j) {
-    float a = -__builtin_huge_valf(), bad = 0.f;
+    float a = -__builtin_huge_valf();
     if (full) {
 #pragma unroll
       for (int i = 0; i < FN; ++i)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          a = fmaxf(a, acc[i][j][r]);
-          bad = fmaf(acc[i][j][r], 0.f, bad);
-        }
+        for (int r = 0; r < 4; ++r) a = fmaxf(a, acc[i][j][r]);
     } else {
 #pragma unroll
       for (int i = 0; i < FN; ++i)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const bool ok = i * 16 + r < lim;
-          a = ok ? fmaxf(a, acc[i][j][r]) : a;
-          bad = ok ? fmaf(acc[i][j][r], 0.f, bad) : bad;
-        }
+        for (int r = 0; r < 4; ++r) a = (i * 16 + r < lim) ? fmaxf(a, acc[i][j][r]) : a;
     }
-    // (a is -inf only for a lane with no column below N, or all logits -inf)
+    // (a is -inf for a lane with no column below N, or whose logits are all
+    // -inf or NaN: its terms are then 0, or NaN)
     const bool any = a != -__builtin_huge_valf();
-    const float m = any ? (BF16 ? bf16_value(a) : a) : a;
+    float m = a, b2 = a;
+    if (BF16 && any) bf16_values(m, b2);
     const float mb = any ? -m * kLog2e : 0.f;
     float s = 0.f;
-    if (full) {
 #pragma unroll
-      for (int i = 0; i < FN; ++i)
+    for (int i = 0; i < FN; ++i)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const float v = BF16 ? bf16_value(acc[i][j][r]) : acc[i][j][r];
-          s += __builtin_amdgcn_exp2f(fmaf(v, kLog2e, mb));
+      for (int r = 0; r < 4; r += 2) {
+        float v0 = acc[i][j][r], v1 = acc[i][j][r + 1];
+        if (BF16) bf16_values(v0, v1);
+        const float e0 = __builtin_amdgcn_exp2f(fmaf(v0, kLog2e, mb));
+        const float e1 = __builtin_amdgcn_exp2f(fmaf(v1, kLog2e, mb));
+        if (full) {
+          s += e0;
+          s += e1;
+        } else {
+          s += (i * 16 + r < lim) ? e0 : 0.f;
+          s += (i * 16 + r + 1 < lim) ? e1 : 0.f;
         }
-    } else {
-#pragma unroll
-      for (int i = 0; i < FN; ++i)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const float v = BF16 ? bf16_value(acc[i][j][r]) : acc[i][j][r];
-          const float e = __builtin_amdgcn_exp2f(fmaf(v, kLog2e, mb));
-          s += (i * 16 + r < lim) ? e : 0.f;
-        }
-    }
-    float m2 = m + bad;  // NaN when an accumulator was NaN or infinite
-    s = any ? s : 0.f;
+      }
+    float m2 = (s != s) ? s : m;  // NaN when a logit was NaN or infinite
     lse_merge(m2, s, __shfl_xor(m2, 16), __shfl_xor(s, 16));
     lse_merge(m2, s, __shfl_xor(m2, 32), __shfl_xor(s, 32));
     mx[j] = m2;
